@@ -1,0 +1,19 @@
+"""Exact IO-aware tiled attention (forward and backward) for AMD MI355X (gfx950).
+
+The compute lives in ``libattn.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/attn.h``).  This package is the thin Python binding:
+``attn_fwd`` / ``attn_bwd`` marshal torch device tensors into that ABI, and
+``forward`` / ``backward`` are conveniences that allocate the outputs.  The
+library is loaded on first use; if it is missing every call raises.
+"""
+
+from ._lib import (  # noqa: F401
+    AttnError,
+    attn_fwd,
+    attn_bwd,
+    attn_bwd_workspace_bytes,
+    forward,
+    backward,
+    library_path,
+    load_library,
+)

@@ -1,0 +1,186 @@
+"""ctypes binding of libattn.so (declared in include/attn.h).
+
+Argument marshalling only: shape/dtype/contiguity checks on torch tensors,
+then raw device pointers, sizes and the current HIP stream go through the C
+ABI.  Every step of the computation runs in the library's HIP kernels.  There
+is no fallback: if the library cannot be loaded, calls raise.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libattn.so"
+_lib = None
+
+ATTN_DTYPE_FP16 = 0
+ATTN_DTYPE_BF16 = 1
+
+# Entry points declared in include/attn.h (checked by the ABI test).
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_strerror",
+           "attn_last_hip_error", "attn_version")
+
+
+class AttnError(RuntimeError):
+    """A libattn call returned a non-zero attn_status_t."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {strerror(status)} (status {status}, "
+                         f"hip error {last_hip_error()})")
+
+
+def library_path() -> str:
+    return os.environ.get("ATTN_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library():
+    """Load libattn.so once and declare its prototypes."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd.restype = i
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
+    lib.attn_bwd.restype = i
+    lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_strerror.argtypes = [i]
+    lib.attn_strerror.restype = ctypes.c_char_p
+    lib.attn_last_hip_error.argtypes = []
+    lib.attn_last_hip_error.restype = i
+    lib.attn_version.argtypes = []
+    lib.attn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def strerror(status: int) -> str:
+    return load_library().attn_strerror(int(status)).decode()
+
+
+def last_hip_error() -> int:
+    return int(load_library().attn_last_hip_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return ATTN_DTYPE_BF16
+    if t.dtype == torch.float16:
+        return ATTN_DTYPE_FP16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float16")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, shape, dtype, device, name):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _dims(q, k):
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B,N,Hq,d] and k/v [B,N,Hkv,d]")
+    b, n, hq, d = q.shape
+    return b, n, hq, k.shape[2], d
+
+
+def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
+    """Enqueue the forward pass into preallocated ``o`` and ``lse``."""
+    import torch
+
+    lib = load_library()
+    b, n, hq, hkv, d = _dims(q, k)
+    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, n, hkv, d), "k"),
+                       (v, (b, n, hkv, d), "v"), (o, (b, n, hq, d), "o")):
+        _check(t, shp, q.dtype, q.device, nm)
+    _check(lse, (b, hq, n), torch.float32, q.device, "lse")
+    st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, n, hq, hkv, d,
+                      _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd")
+
+
+def attn_bwd_workspace_bytes(b: int, n: int, hq: int, hkv: int, d: int) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(b, n, hq, hkv, d))
+
+
+def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
+             stream=None) -> None:
+    """Enqueue the backward pass into preallocated ``dq``, ``dk``, ``dv``.
+
+    ``workspace`` is a uint8 device tensor of at least
+    ``attn_bwd_workspace_bytes(B, N, Hq, Hkv, d)`` bytes.
+    """
+    import torch
+
+    lib = load_library()
+    b, n, hq, hkv, d = _dims(q, k)
+    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, n, hkv, d), "k"),
+                       (v, (b, n, hkv, d), "v"), (o, (b, n, hq, d), "o"),
+                       (dout, (b, n, hq, d), "dout"), (dq, (b, n, hq, d), "dq"),
+                       (dk, (b, n, hkv, d), "dk"), (dv, (b, n, hkv, d), "dv")):
+        _check(t, shp, q.dtype, q.device, nm)
+    _check(lse, (b, hq, n), torch.float32, q.device, "lse")
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                      _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, b, n, hq, hkv, d,
+                      _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd")
+
+
+def _default_scale(d: int, scale):
+    return 1.0 / math.sqrt(d) if scale is None else float(scale)
+
+
+def forward(q, k, v, causal: bool = False, scale=None, stream=None):
+    """Allocate ``o`` and ``lse`` and run ``attn_fwd``; returns (o, lse)."""
+    import torch
+
+    b, n, hq, _, d = _dims(q, k)
+    o = torch.empty_like(q)
+    lse = torch.empty((b, hq, n), dtype=torch.float32, device=q.device)
+    attn_fwd(q, k, v, o, lse, causal, _default_scale(d, scale), stream)
+    return o, lse
+
+
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale=None, stream=None, workspace=None):
+    """Allocate gradients (and the workspace if not given) and run ``attn_bwd``."""
+    import torch
+
+    b, n, hq, hkv, d = _dims(q, k)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    if workspace is None:
+        workspace = torch.empty(attn_bwd_workspace_bytes(b, n, hq, hkv, d), dtype=torch.uint8,
+                                device=q.device)
+    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, _default_scale(d, scale), stream)
+    return dq, dk, dv

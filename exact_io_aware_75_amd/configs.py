@@ -1,0 +1,79 @@
+"""Workload shapes and throughput accounting.
+
+The shapes restate the measured grid the pages describe: sequence lengths
+512..16k with an attention layer of hidden size 2048 and head dimension 64 or
+128, causal and not (FlashAttention-2 announcement, "实验评估" section;
+FlashAttention-2 review, "Результаты" section -- both say "64 or 128 heads",
+which with hidden size 2048 can only mean head dimension 64 or 128); head
+dimension up to 256 and MQA/GQA ("具体实现" section); long sequences up to 64k
+(FlashAttention-1 news page, results on block-sparse attention at 64k).
+
+FLOP accounting: forward 4*B*Hq*N^2*d (two N x N x d products), halved under a
+causal mask; backward 2.5 x forward (five products instead of two).
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, asdict
+
+SWEEP_N = (512, 1024, 2048, 4096, 8192, 16384)
+TOKENS = 16384  # B * N for the hidden-size-2048 sweep
+
+
+@dataclass(frozen=True)
+class Shape:
+    name: str
+    cfg_id: int
+    b: int
+    n: int
+    hq: int
+    hkv: int
+    d: int
+    dtype: str
+    causal: bool
+
+    def fwd_flops(self) -> float:
+        f = 4.0 * self.b * self.hq * self.n * self.n * self.d
+        return f / 2 if self.causal else f
+
+    def bwd_flops(self) -> float:
+        return 2.5 * self.fwd_flops()
+
+    def as_dict(self):
+        return asdict(self)
+
+
+def small_fp16() -> Shape:
+    """Forward-only parity case: B=1, H=2, N=128, d=64, fp16, non-causal."""
+    return Shape("fwd_small_fp16", 1, 1, 128, 2, 2, 64, "fp16", False)
+
+
+def hidden2048(d: int, n: int, causal: bool) -> Shape:
+    """Hidden size 2048 (H = 2048/d), B*N = 16384 tokens, bf16."""
+    return Shape(f"h2048_d{d}", 2 if d == 64 else 3, TOKENS // n, n, 2048 // d, 2048 // d,
+                 d, "bf16", causal)
+
+
+def long_seq(n: int) -> Shape:
+    """B=1, H=8, d=128, causal, N in {32768, 65536}."""
+    return Shape("long_seq", 4, 1, n, 8, 8, 128, "bf16", True)
+
+
+def gqa(hkv: int) -> Shape:
+    """B=4, N=4096, Hq=32, Hkv in {8, 1}, d=128, causal."""
+    return Shape(f"gqa_hkv{hkv}", 5, 4, 4096, 32, hkv, 128, "bf16", True)
+
+
+def wide_head() -> Shape:
+    """B=4, N=4096, H=8, d=256, causal (MHA)."""
+    return Shape("mha_d256", 5, 4, 4096, 8, 8, 256, "bf16", True)
+
+
+def all_shapes():
+    out = [small_fp16()]
+    for d in (64, 128):
+        for n in SWEEP_N:
+            for c in (False, True):
+                out.append(hidden2048(d, n, c))
+    out += [long_seq(32768), long_seq(65536), gqa(8), gqa(1), wide_head()]
+    return out

@@ -1,0 +1,126 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact, IO-aware tiled attention (forward and
+ * backward) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  Exact scaled-dot-product attention, the same result as
+ * standard attention up to rounding (FlashAttention-2 review, "Введение"
+ * section: the tiled algorithm is mathematically equivalent to attention up to
+ * numerical precision).  For query head h and its K/V head g = h / (Hq/Hkv):
+ *
+ *     S = scale * Q K^T,   P = softmax(S) row-wise,   O = P V,
+ *     LSE[i] = ln sum_j exp(S[i, j])          (natural log, per query row)
+ *
+ * with keys j > i excluded when `causal` is set.  The N x N matrices S and P
+ * never reach device memory: the forward pass streams K/V tiles through LDS
+ * and keeps an online softmax in registers (tiling from HBM into on-chip
+ * memory: FlashAttention-2 announcement, "具体实现" section; FlashAttention-1
+ * news page, "FlashAttention" section).  The backward pass recomputes P tile
+ * by tile from Q, K, V and LSE instead of storing it (same sections), and
+ * produces dQ, dK, dV of L = sum(O * dO).  MQA/GQA (Hkv < Hq) and head
+ * dimensions up to 256 follow the same announcement's "具体实现" section.
+ *
+ * Tensor layout.  All tensors are dense, row-major, device-resident:
+ *     q, o, dout, dq : [B, N, Hq,  d]     (d innermost)
+ *     k, v, dk, dv   : [B, N, Hkv, d]
+ *     lse            : [B, Hq, N] float32
+ * q, k, v, o, dout, dq, dk, dv share one element type (`dtype`).  Every
+ * pointer must be 16-byte aligned.  Consecutive query heads share a K/V head
+ * (query head h reads K/V head h / (Hq / Hkv)).  Supported head dimensions are
+ * d = 64, 128 and 256; any N >= 1 is accepted (partial tiles are masked).
+ *
+ * Ownership and ordering.  All buffers are owned by the caller.  The library
+ * never allocates or frees device memory and keeps no state besides a
+ * per-device property cache and a thread-local last-HIP-error code.  Work is
+ * enqueued on `stream` (a hipStream_t; NULL means the legacy default stream)
+ * and calls return without synchronising; the caller keeps every buffer alive
+ * until the stream has finished.  Outputs must not alias inputs.  Calls that
+ * share a backward workspace must be ordered on one stream.
+ *
+ * Errors.  Each entry point returns an attn_status_t.  Arguments are
+ * validated before anything is launched; on any error nothing is written.
+ * A failed launch returns ATTN_ERR_HIP and attn_last_hip_error() gives the
+ * hipError_t of the failing call on this thread.
+ */
+#ifndef ATTN_H_
+#define ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_DTYPE_FP16 = 0, /* IEEE binary16 */
+  ATTN_DTYPE_BF16 = 1  /* bfloat16 */
+} attn_dtype_t;
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_NULLPTR = 1,   /* a required pointer is NULL */
+  ATTN_ERR_SHAPE = 2,     /* B, N, Hq, Hkv < 1, or Hq not a multiple of Hkv */
+  ATTN_ERR_HEADDIM = 3,   /* d not in {64, 128, 256} */
+  ATTN_ERR_DTYPE = 4,     /* dtype not an attn_dtype_t */
+  ATTN_ERR_ALIGN = 5,     /* a pointer is not 16-byte aligned */
+  ATTN_ERR_SCALE = 6,     /* scale is NaN or infinite */
+  ATTN_ERR_WORKSPACE = 7, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
+  ATTN_ERR_DEVICE = 8,    /* no current HIP device, or it is not gfx950 */
+  ATTN_ERR_HIP = 9,       /* a HIP launch failed; see attn_last_hip_error() */
+  ATTN_ERR_TOO_LARGE = 10 /* a tensor has 2^31 or more elements per (batch, head) slice,
+                             or the launch grid would exceed the device limits */
+} attn_status_t;
+
+/*
+ * Forward pass.  Writes o = softmax(scale * q k^T [causal mask]) v and the
+ * per-row natural-log log-sum-exp `lse` (saved for the backward pass's
+ * recomputation).  Accumulation is fp32; o is rounded to nearest-even into
+ * `dtype`.
+ *
+ *   q [B,N,Hq,d], k/v [B,N,Hkv,d]   inputs, dtype
+ *   o [B,N,Hq,d]                    output, dtype
+ *   lse [B,Hq,N]                    output, float32
+ *   causal                          nonzero: query i attends keys j <= i only
+ *   scale                           multiplies q k^T (typically 1/sqrt(d)); 0 is legal
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int N, int Hq, int Hkv, int d, int dtype, int causal, float scale,
+             void* stream);
+
+/*
+ * Bytes of device workspace attn_bwd needs for these sizes: an fp32 dQ
+ * accumulator and the per-row D = rowsum(dO * O), both O(B * N * Hq * d), plus
+ * alignment.  Returns 0 if the sizes are invalid.
+ */
+size_t attn_bwd_workspace_bytes(int B, int N, int Hq, int Hkv, int d);
+
+/*
+ * Backward pass.  Given the forward inputs, its outputs o and lse (from an
+ * attn_fwd call with the same causal flag and scale) and the upstream gradient
+ * dout, writes dq, dk, dv of L = sum(o * dout).  Scores and probabilities are
+ * recomputed tile by tile from lse; the work is parallel over key/value
+ * column blocks.  dk/dv of a K/V head sum the contributions of every query
+ * head in its group.  `workspace` (device memory, 16-byte aligned, at least
+ * attn_bwd_workspace_bytes() bytes) is scratch: its contents on entry are
+ * ignored and on exit undefined.  Results are deterministic up to the order of
+ * fp32 atomic additions in the dQ accumulator.
+ */
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
+             int causal, float scale, void* stream);
+
+/* Static, human-readable description of a status code. */
+const char* attn_strerror(int status);
+
+/* hipError_t of the last failed HIP call made by this library on this thread
+ * (0 if none). */
+int attn_last_hip_error(void);
+
+/* Library version string. */
+const char* attn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H_ */

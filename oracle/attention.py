@@ -1,0 +1,185 @@
+"""Plain fp64 attention: the definition the tiled method must reproduce.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+Sources.  The pages state that the IO-aware method is exact -- mathematically
+equivalent, up to numerical precision, to standard attention (FlashAttention-2
+review, "Введение" section; FlashAttention-1 news page, "FlashAttention"
+section, which calls it an "exact attention algorithm") -- and that standard
+attention materialises the N x N score matrix (FlashAttention-1 news page,
+"FlashAttention" section; FlashAttention-2 announcement, "具体实现" section).
+The backward pass recomputes that matrix block by block (same sections); here
+it is recomputed whole, row chunk by row chunk, and differentiated
+analytically.  The pages print no formulas, so the formulas below are the
+textbook definition of softmax attention and its gradient:
+
+forward, for one query head h with key/value head g:
+    S[i, j]   = scale * <Q[i], K[j]>
+    allowed   = (not causal) or (j <= i)          rows are queries, columns keys
+    m_i       = max_{allowed j} S[i, j]
+    e[i, j]   = exp(S[i, j] - m_i) if allowed else 0
+    l_i       = sum_j e[i, j]
+    P[i, j]   = e[i, j] / l_i
+    O[i]      = sum_j P[i, j] V[j]
+    LSE[i]    = m_i + ln l_i                      natural logarithm
+
+backward, with upstream gradient dO (loss L = sum O * dO):
+    dP[i, j]  = <dO[i], V[j]>
+    D_i       = sum_j P[i, j] dP[i, j]            by this definition, not dO . O
+    dS[i, j]  = P[i, j] (dP[i, j] - D_i)
+    dQ[i]     = scale * sum_j dS[i, j] K[j]
+    dK[j]     = scale * sum_{h in group} sum_i dS[i, j] Q[i]
+    dV[j]     = sum_{h in group} sum_i P[i, j] dO[i]
+
+Readings where the pages are silent (listed again in the design doc):
+  * causal orientation: query i may attend key j iff j <= i (the pages only
+    say the masked triangle is skipped rather than computed and zeroed;
+    FlashAttention-2 review, "Алгоритм вычисления" subsection);
+  * GQA/MQA (named, not defined, in the FlashAttention-2 announcement,
+    "具体实现" section): query head h reads K/V head h // (Hq / Hkv), i.e.
+    consecutive query heads share a K/V head;
+  * a row with no allowed key (impossible when Nq = Nk) has O = 0 and
+    LSE = -inf;
+  * LSE is the natural-log log-sum-exp of the scaled scores.
+
+Layouts: Q, O, dO, dQ are [B, N, Hq, d]; K, V, dK, dV are [B, N, Hkv, d];
+LSE is [B, Hq, N].  Every input is upcast to float64; nothing is rounded on
+the way out.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+_F = np.float64
+
+
+def kv_head_of(h: int, hq: int, hkv: int) -> int:
+    """K/V head read by query head ``h`` (consecutive groups of Hq/Hkv heads)."""
+    if hkv <= 0 or hq % hkv != 0:
+        raise ValueError(f"Hq={hq} must be a positive multiple of Hkv={hkv}")
+    return h // (hq // hkv)
+
+
+def _allowed(rows: np.ndarray, n_keys: int, causal: bool) -> np.ndarray:
+    """Boolean [len(rows), n_keys] mask: key j visible to query row i."""
+    cols = np.arange(n_keys)
+    if not causal:
+        return np.ones((len(rows), n_keys), dtype=bool)
+    return cols[None, :] <= rows[:, None]
+
+
+def _row_softmax(s: np.ndarray, allowed: np.ndarray):
+    """Max-subtracted softmax of each row over its allowed entries.
+
+    Returns (P, lse).  Rows with no allowed entry give P = 0 and lse = -inf.
+    """
+    masked = np.where(allowed, s, -np.inf)
+    m = masked.max(axis=1)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    e = np.where(allowed, np.exp(masked - m_safe[:, None]), 0.0)
+    l = e.sum(axis=1)
+    l_safe = np.where(empty, 1.0, l)
+    p = e / l_safe[:, None]
+    lse = np.where(empty, -np.inf, m_safe + np.log(l_safe))
+    return p, lse
+
+
+def attention_head_probs(q, k, causal: bool, scale: float) -> np.ndarray:
+    """Full probability matrix P [Nq, Nk] of one head (small inputs only)."""
+    q = np.asarray(q, dtype=_F)
+    k = np.asarray(k, dtype=_F)
+    s = scale * (q @ k.T)
+    p, _ = _row_softmax(s, _allowed(np.arange(q.shape[0]), k.shape[0], causal))
+    return p
+
+
+def attention_head_fwd(q, k, v, causal: bool, scale: float, rows=None, chunk: int = 512):
+    """O and LSE of one head for the query ``rows`` (default: all rows).
+
+    q: [N, d] all query rows of the head; k, v: [N, d] of its K/V head.
+    Rows are independent, so they are processed in chunks of whole rows.
+    """
+    q = np.asarray(q, dtype=_F)
+    k = np.asarray(k, dtype=_F)
+    v = np.asarray(v, dtype=_F)
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((len(rows), v.shape[1]), dtype=_F)
+    lse = np.empty(len(rows), dtype=_F)
+    for c0 in range(0, len(rows), chunk):
+        r = rows[c0:c0 + chunk]
+        s = scale * (q[r] @ k.T)
+        p, lse[c0:c0 + chunk] = _row_softmax(s, _allowed(r, k.shape[0], causal))
+        o[c0:c0 + chunk] = p @ v
+    return o, lse
+
+
+def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk: int = 512):
+    """Gradients of L = sum(O * dO) for one query head.
+
+    Returns (dq_rows, dk, dv): dq for the query ``rows`` (default: all) and this
+    head's whole contribution to dK and dV of its K/V head.  dK/dV need every
+    query row, so they are only returned when ``rows`` is None.
+    """
+    q = np.asarray(q, dtype=_F)
+    k = np.asarray(k, dtype=_F)
+    v = np.asarray(v, dtype=_F)
+    do = np.asarray(do, dtype=_F)
+    full = rows is None
+    rows = np.arange(q.shape[0]) if full else np.asarray(rows, dtype=np.int64)
+    dq = np.empty((len(rows), q.shape[1]), dtype=_F)
+    dk = np.zeros_like(k) if full else None
+    dv = np.zeros_like(v) if full else None
+    for c0 in range(0, len(rows), chunk):
+        r = rows[c0:c0 + chunk]
+        s = scale * (q[r] @ k.T)
+        p, _ = _row_softmax(s, _allowed(r, k.shape[0], causal))
+        dp = do[r] @ v.T
+        dsum = (p * dp).sum(axis=1)
+        ds = p * (dp - dsum[:, None])
+        dq[c0:c0 + chunk] = scale * (ds @ k)
+        if full:
+            dk += scale * (ds.T @ q[r])
+            dv += p.T @ do[r]
+    return dq, dk, dv
+
+
+def _check_shapes(q, k, v):
+    if q.ndim != 4 or k.shape != v.shape or k.ndim != 4:
+        raise ValueError("expected q [B,N,Hq,d] and k, v [B,N,Hkv,d]")
+    b, n, hq, d = q.shape
+    if k.shape[0] != b or k.shape[1] != n or k.shape[3] != d:
+        raise ValueError("q and k/v disagree in B, N or d")
+    return b, n, hq, k.shape[2], d
+
+
+def attention_fwd(q, k, v, causal: bool, scale: float):
+    """O [B,N,Hq,d] and LSE [B,Hq,N] in float64."""
+    b, n, hq, hkv, d = _check_shapes(q, k, v)
+    o = np.empty((b, n, hq, d), dtype=_F)
+    lse = np.empty((b, hq, n), dtype=_F)
+    for bi in range(b):
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            o[bi, :, h], lse[bi, h] = attention_head_fwd(
+                q[bi, :, h], k[bi, :, g], v[bi, :, g], causal, scale)
+    return o, lse
+
+
+def attention_bwd(q, k, v, do, causal: bool, scale: float):
+    """(dQ, dK, dV) in float64; dK/dV sum the contributions of each group."""
+    b, n, hq, hkv, d = _check_shapes(q, k, v)
+    dq = np.empty((b, n, hq, d), dtype=_F)
+    dk = np.zeros((b, n, hkv, d), dtype=_F)
+    dv = np.zeros((b, n, hkv, d), dtype=_F)
+    for bi in range(b):
+        for h in range(hq):
+            g = kv_head_of(h, hq, hkv)
+            dqh, dkh, dvh = attention_head_bwd(
+                q[bi, :, h], k[bi, :, g], v[bi, :, g], do[bi, :, h], causal, scale)
+            dq[bi, :, h] = dqh
+            dk[bi, :, g] += dkh
+            dv[bi, :, g] += dvh
+    return dq, dk, dv

@@ -1,0 +1,312 @@
+"""Pins for the CPU fp64 oracle: nothing here compares the oracle with itself.
+
+Each test ties the oracle to something fixed independently of it: finite
+differences, PyTorch's own fp64 scaled_dot_product_attention + autograd,
+closed forms, invariants of softmax attention, a hand-derived example, and the
+tiled online-softmax model (the pages' claim that block-wise computation with
+aggregation equals standard attention up to numerical precision --
+FlashAttention-2 review, "Введение" section).  Planted mistakes at the end
+check that these pins actually catch the usual slips.
+"""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import attention as oa
+from exact_io_aware_75_amd.inputs import make_inputs, round_to_bf16
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+def _loss(q, k, v, do, causal, scale):
+    o, _ = oracle.attention_fwd(q, k, v, causal, scale)
+    return float((o * do).sum())
+
+
+def _fd_grads(q, k, v, do, causal, scale, h=1e-6):
+    grads = []
+    for which in range(3):
+        base = [q, k, v]
+        x = base[which]
+        g = np.zeros_like(x)
+        it = np.nditer(x, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            xp = x.copy(); xp[idx] += h
+            xm = x.copy(); xm[idx] -= h
+            args_p = list(base); args_p[which] = xp
+            args_m = list(base); args_m[which] = xm
+            g[idx] = (_loss(*args_p, do, causal, scale) - _loss(*args_m, do, causal, scale)) / (2 * h)
+        grads.append(g)
+    return grads
+
+
+def _rel(a, b):
+    return np.abs(a - b).max() / max(np.abs(b).max(), 1e-30)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradients_match_finite_differences(causal):
+    """Brute force: central differences of L = sum(O * dO) at N=8, d=4, Hq=2, Hkv=1."""
+    q, k, v, do = _rand((1, 8, 2, 4), 1), _rand((1, 8, 1, 4), 2), _rand((1, 8, 1, 4), 3), _rand((1, 8, 2, 4), 4)
+    scale = 0.7
+    dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, scale)
+    fq, fk, fv = _fd_grads(q, k, v, do, causal, scale)
+    assert _rel(dq, fq) < 1e-6
+    assert _rel(dk, fk) < 1e-6
+    assert _rel(dv, fv) < 1e-6
+
+
+def _torch_ref(q, k, v, do, causal, scale):
+    """PyTorch CPU fp64 scaled_dot_product_attention + autograd (a library
+    implementation of the same definition).  GQA through repeat_interleave."""
+    import torch
+
+    hq, hkv = q.shape[2], k.shape[2]
+    tq = torch.tensor(q).permute(0, 2, 1, 3).contiguous().requires_grad_()
+    tk = torch.tensor(k).permute(0, 2, 1, 3).contiguous().requires_grad_()
+    tv = torch.tensor(v).permute(0, 2, 1, 3).contiguous().requires_grad_()
+    kk = tk.repeat_interleave(hq // hkv, dim=1)
+    vv = tv.repeat_interleave(hq // hkv, dim=1)
+    o = torch.nn.functional.scaled_dot_product_attention(tq, kk, vv, is_causal=causal, scale=scale)
+    o.backward(torch.tensor(do).permute(0, 2, 1, 3))
+    s = scale * (tq.detach() @ kk.detach().transpose(-1, -2))
+    if causal:
+        n = q.shape[1]
+        s = s.masked_fill(torch.ones(n, n, dtype=torch.bool).triu(1), float("-inf"))
+    lse = torch.logsumexp(s, dim=-1)
+    to_np = lambda t: t.detach().permute(0, 2, 1, 3).numpy()  # noqa: E731
+    return to_np(o), lse.numpy(), to_np(tq.grad), to_np(tk.grad), to_np(tv.grad)
+
+
+@pytest.mark.parametrize("b,n,hq,hkv,d,causal", [
+    (1, 33, 2, 2, 16, False),
+    (2, 40, 4, 2, 8, True),
+    (1, 65, 4, 1, 32, True),
+    (1, 64, 3, 3, 64, False),
+])
+def test_matches_torch_sdpa_fp64(b, n, hq, hkv, d, causal):
+    x = make_inputs(b, n, hq, hkv, d, "bf16", cfg_id=99, seed=n)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = oracle.attention_fwd(x["q"], x["k"], x["v"], causal, scale)
+    dq, dk, dv = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], causal, scale)
+    to, tlse, tdq, tdk, tdv = _torch_ref(*(x[t].astype(np.float64) for t in ("q", "k", "v", "do")), causal, scale)
+    for a, r in ((o, to), (lse, tlse), (dq, tdq), (dk, tdk), (dv, tdv)):
+        assert np.abs(a - r).max() < 1e-12
+
+
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_n2_d1.json")))
+    q = np.array(g["q"]).reshape(1, 2, 1, 1)
+    k = np.array(g["k"]).reshape(1, 2, 1, 1)
+    v = np.array(g["v"]).reshape(1, 2, 1, 1)
+    do = np.array(g["do"]).reshape(1, 2, 1, 1)
+    for key, causal in (("noncausal", False), ("causal", True)):
+        exp = g[key]
+        o, lse = oracle.attention_fwd(q, k, v, causal, 1.0)
+        dq, dk, dv = oracle.attention_bwd(q, k, v, do, causal, 1.0)
+        np.testing.assert_allclose(o.ravel(), exp["o"], atol=1e-14)
+        np.testing.assert_allclose(lse.ravel(), exp["lse"], atol=1e-14)
+        np.testing.assert_allclose(dq.ravel(), exp["dq"], atol=1e-14)
+        np.testing.assert_allclose(dk.ravel(), exp["dk"], atol=1e-14)
+        np.testing.assert_allclose(dv.ravel(), exp["dv"], atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_softmax_rows_sum_to_one(causal):
+    x = make_inputs(1, 50, 1, 1, 16, "bf16", cfg_id=98)
+    p = oracle.attention_head_probs(x["q"][0, :, 0], x["k"][0, :, 0], causal, 0.25)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, atol=1e-12)
+    assert (p >= 0).all()
+    if causal:
+        assert (np.triu(p, 1) == 0).all()
+
+
+def _n_allowed(n, causal):
+    return np.arange(1, n + 1) if causal else np.full(n, n)
+
+
+def _prefix_mean(v, causal):
+    if causal:
+        return np.cumsum(v, axis=0) / np.arange(1, v.shape[0] + 1)[:, None]
+    return np.broadcast_to(v.mean(axis=0), v.shape)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_give_mean_of_values(causal):
+    n, d = 37, 8
+    q, v = _rand((1, n, 1, d), 5), _rand((1, n, 1, d), 6)
+    k = np.broadcast_to(_rand((1, 1, 1, d), 7), (1, n, 1, d)).copy()
+    scale = 0.3
+    o, lse = oracle.attention_fwd(q, k, v, causal, scale)
+    np.testing.assert_allclose(o[0, :, 0], _prefix_mean(v[0, :, 0], causal), atol=1e-12)
+    s0 = scale * (q[0, :, 0] @ k[0, 0, 0])
+    np.testing.assert_allclose(lse[0, 0], s0 + np.log(_n_allowed(n, causal)), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_scale_is_uniform(causal):
+    n, d = 29, 4
+    x = make_inputs(1, n, 2, 1, d, "bf16", cfg_id=97)
+    o, lse = oracle.attention_fwd(x["q"], x["k"], x["v"], causal, 0.0)
+    for h in range(2):
+        np.testing.assert_allclose(o[0, :, h], _prefix_mean(x["v"][0, :, 0].astype(np.float64), causal), atol=1e-12)
+        np.testing.assert_allclose(lse[0, h], np.log(_n_allowed(n, causal)), atol=1e-13)
+
+
+def test_causal_first_row():
+    x = make_inputs(2, 19, 2, 2, 8, "bf16", cfg_id=96)
+    scale = 0.5
+    o, lse = oracle.attention_fwd(x["q"], x["k"], x["v"], True, scale)
+    dq, _, _ = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], True, scale)
+    np.testing.assert_allclose(o[:, 0], x["v"][:, 0], atol=1e-14)
+    s00 = scale * np.einsum("bhd,bhd->bh", x["q"][:, 0].astype(np.float64), x["k"][:, 0].astype(np.float64))
+    np.testing.assert_allclose(lse[:, :, 0], s00, atol=1e-12)
+    assert np.abs(dq[:, 0]).max() == 0.0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_token(causal):
+    x = make_inputs(3, 1, 4, 2, 16, "bf16", cfg_id=95)
+    o, lse = oracle.attention_fwd(x["q"], x["k"], x["v"], causal, 0.25)
+    dq, dk, dv = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], causal, 0.25)
+    np.testing.assert_allclose(o, np.repeat(x["v"], 2, axis=2), atol=1e-14)
+    assert np.abs(dq).max() == 0 and np.abs(dk).max() == 0
+    np.testing.assert_allclose(dv, x["do"].reshape(3, 1, 2, 2, 16).sum(axis=3), atol=1e-14)
+
+
+@pytest.mark.parametrize("hkv", [1, 2])
+def test_gqa_equals_mha_with_repeated_heads(hkv):
+    b, n, hq, d = 2, 23, 4, 8
+    x = make_inputs(b, n, hq, hkv, d, "bf16", cfg_id=94)
+    rep = hq // hkv
+    k2, v2 = np.repeat(x["k"], rep, axis=2), np.repeat(x["v"], rep, axis=2)
+    for causal in (False, True):
+        o, lse = oracle.attention_fwd(x["q"], x["k"], x["v"], causal, 0.35)
+        om, lsem = oracle.attention_fwd(x["q"], k2, v2, causal, 0.35)
+        np.testing.assert_allclose(o, om, atol=1e-14)
+        np.testing.assert_allclose(lse, lsem, atol=1e-14)
+        dq, dk, dv = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], causal, 0.35)
+        dqm, dkm, dvm = oracle.attention_bwd(x["q"], k2, v2, x["do"], causal, 0.35)
+        np.testing.assert_allclose(dq, dqm, atol=1e-14)
+        np.testing.assert_allclose(dk, dkm.reshape(b, n, hkv, rep, d).sum(axis=3), atol=1e-13)
+        np.testing.assert_allclose(dv, dvm.reshape(b, n, hkv, rep, d).sum(axis=3), atol=1e-13)
+
+
+def test_noncausal_permutation_invariance():
+    n, d = 31, 8
+    x = make_inputs(1, n, 2, 2, d, "bf16", cfg_id=93)
+    perm = np.random.default_rng(0).permutation(n)
+    o, lse = oracle.attention_fwd(x["q"], x["k"], x["v"], False, 0.4)
+    o_kv, _ = oracle.attention_fwd(x["q"], x["k"][:, perm], x["v"][:, perm], False, 0.4)
+    o_q, lse_q = oracle.attention_fwd(x["q"][:, perm], x["k"], x["v"], False, 0.4)
+    np.testing.assert_allclose(o_kv, o, atol=1e-13)
+    np.testing.assert_allclose(o_q, o[:, perm], atol=1e-14)
+    np.testing.assert_allclose(lse_q, lse[:, :, perm], atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_gradient_identities(causal):
+    """sum_j dV_j = sum_{h in group} sum_i dO_i;  sum_j dK_j = 0;
+    sum <Q, dQ> = sum <K, dK> (scores are bilinear in Q and K)."""
+    b, n, hq, hkv, d = 2, 45, 4, 2, 16
+    x = make_inputs(b, n, hq, hkv, d, "bf16", cfg_id=92)
+    dq, dk, dv = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], causal, 0.25)
+    dsum = x["do"].astype(np.float64).reshape(b, n, hkv, hq // hkv, d).sum(axis=(1, 3))
+    np.testing.assert_allclose(dv.sum(axis=1), dsum, atol=1e-11)
+    assert np.abs(dk.sum(axis=1)).max() < 1e-12
+    lhs = np.einsum("bnhd,bnhd->b", x["q"].astype(np.float64), dq)
+    rhs = np.einsum("bnhd,bnhd->b", x["k"].astype(np.float64), dk)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-11, atol=1e-11)
+
+
+@pytest.mark.parametrize("n,bm,bn,causal", [
+    (64, 16, 16, False), (64, 16, 16, True), (100, 16, 32, True),
+    (129, 32, 16, False), (129, 32, 16, True), (7, 16, 16, True),
+])
+def test_tiled_online_softmax_equals_standard(n, bm, bn, causal):
+    """The pages' equivalence claim, in fp64: block-wise aggregation = standard."""
+    x = make_inputs(1, n, 1, 1, 32, "bf16", cfg_id=91, seed=n)
+    q, k, v = x["q"][0, :, 0], x["k"][0, :, 0], x["v"][0, :, 0]
+    o, lse, visited = oracle.tiled_attention_fwd(q, k, v, causal, 0.2, bm=bm, bn=bn)
+    o_ref, lse_ref = oracle.attention_head_fwd(q, k, v, causal, 0.2)
+    assert np.abs(o - o_ref).max() < 1e-12
+    assert np.abs(lse - lse_ref).max() < 1e-12
+    nb_q, nb_k = -(-n // bm), -(-n // bn)
+    if causal:  # key block j is visited by row block i iff its first key <= the block's last row
+        expect = sum(min(nb_k, (min(i * bm + bm, n) - 1) // bn + 1) for i in range(nb_q))
+    else:
+        expect = nb_q * nb_k
+    assert visited == expect
+
+
+def test_row_subset_matches_full():
+    x = make_inputs(1, 70, 1, 1, 16, "bf16", cfg_id=90)
+    q, k, v, do = (x[t][0, :, 0] for t in ("q", "k", "v", "do"))
+    rows = np.array([0, 5, 69, 33])
+    o, lse = oracle.attention_head_fwd(q, k, v, True, 0.3)
+    o_r, lse_r = oracle.attention_head_fwd(q, k, v, True, 0.3, rows=rows)
+    assert np.array_equal(o_r, o[rows]) and np.array_equal(lse_r, lse[rows])
+    dq, _, _ = oracle.attention_head_bwd(q, k, v, do, True, 0.3)
+    dq_r, dk_r, dv_r = oracle.attention_head_bwd(q, k, v, do, True, 0.3, rows=rows)
+    np.testing.assert_allclose(dq_r, dq[rows], atol=1e-15)
+    assert dk_r is None and dv_r is None
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.005859375, -2.0078125, 3.0e-3], dtype=np.float32)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7 -> even (1); 1 + 1.5*2^-8 rounds up.
+    r = round_to_bf16(x)
+    assert r[0] == 1.0 and r[1] == 1.0 and r[2] == np.float32(1.0078125)
+    assert r[3] == np.float32(-2.0)  # -2 - 2^-7 is a tie between -2 and -2 - 2^-6 -> even
+    import torch
+
+    t = torch.tensor(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(r, t)
+
+
+# ---- planted mistakes: each mutated oracle must fail at least one pin ----
+
+def _bwd_mutant(kind):
+    def bwd(q, k, v, do, causal, scale, rows=None, chunk=512):
+        q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
+        r = np.arange(q.shape[0])
+        s = scale * (q @ k.T)
+        p, _ = oa._row_softmax(s, oa._allowed(r, k.shape[0], causal))
+        dp = do @ v.T
+        dsum = (p * dp).sum(axis=1)
+        if kind == "drop_D":
+            dsum = 0 * dsum
+        ds = p * (dp - dsum[:, None])
+        sc = 1.0 if kind == "no_scale" else scale
+        dq = sc * (ds @ k)
+        dk = scale * ((ds if kind != "transpose" else ds.T).T @ q)
+        dv = p.T @ do
+        return dq, dk, dv
+    return bwd
+
+
+@pytest.mark.parametrize("kind", ["drop_D", "no_scale", "transpose"])
+def test_planted_backward_mistakes_are_caught(kind, monkeypatch):
+    monkeypatch.setattr(oa, "attention_head_bwd", _bwd_mutant(kind))
+    q, k, v, do = _rand((1, 6, 1, 3), 11), _rand((1, 6, 1, 3), 12), _rand((1, 6, 1, 3), 13), _rand((1, 6, 1, 3), 14)
+    dq, dk, dv = oa.attention_bwd(q, k, v, do, False, 0.6)
+    fq, fk, fv = _fd_grads(q, k, v, do, False, 0.6)
+    assert max(_rel(dq, fq), _rel(dk, fk), _rel(dv, fv)) > 1e-3
+
+
+def test_planted_forward_mistake_is_caught(monkeypatch):
+    """A softmax that forgets the causal mask fails the causal-row-0 closed form."""
+    real = oa._allowed
+    monkeypatch.setattr(oa, "_allowed", lambda rows, n, causal: real(rows, n, False))
+    x = make_inputs(1, 9, 1, 1, 4, "bf16", cfg_id=89)
+    o, _ = oa.attention_fwd(x["q"], x["k"], x["v"], True, 0.5)
+    assert np.abs(o[0, 0] - x["v"][0, 0]).max() > 1e-6
