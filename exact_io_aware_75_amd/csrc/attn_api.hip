@@ -1,0 +1,182 @@
+// C-ABI layer of libattn.so (declared in include/attn.h): argument
+// validation, device check, workspace layout and dispatch to the kernels.
+// No device memory is allocated here; every launch goes on the caller's stream.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/attn.h"
+#include "attn_kernels.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+// 0 = unknown, 1 = gfx950, 2 = other architecture
+std::atomic<int> g_arch_ok[kMaxDevices];
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(int B, int N, int Hq, int Hkv, int d) {
+  if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
+  if (d != 64 && d != 128 && d != 256) return ATTN_ERR_HEADDIM;
+  // element offsets inside one (batch, head) slice and the row-block grid stay in int range
+  if ((long long)N * Hq * d >= (1LL << 31) || (long long)B * Hq * ((N + 127) / 128) >= (1LL << 31))
+    return ATTN_ERR_TOO_LARGE;
+  return ATTN_OK;
+}
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    int known = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (known == 1) return ATTN_OK;
+    if (known == 2) return ATTN_ERR_DEVICE;
+  }
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_DEVICE;
+  }
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+  if (dev < kMaxDevices) g_arch_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+  return ok ? ATTN_OK : ATTN_ERR_DEVICE;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace attn {
+
+BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int /*Hkv*/, int d) {
+  BwdWorkspace w;
+  w.dq_acc_off = 0;
+  w.dq_acc_bytes = (size_t)B * N * Hq * d * sizeof(float);
+  w.delta_off = align256(w.dq_acc_bytes);
+  w.delta_bytes = (size_t)B * Hq * N * sizeof(float);
+  w.total = align256(w.delta_off + w.delta_bytes);
+  return w;
+}
+
+}  // namespace attn
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int N,
+             int Hq, int Hkv, int d, int dtype, int causal, float scale, void* stream) {
+  if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULLPTR;
+  int st = check_shape(B, N, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
+    return ATTN_ERR_ALIGN;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+
+  attn::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.N = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.neg_scale = scale < 0.f ? 1 : 0;
+  a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+  hipError_t e = attn::launch_fwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+size_t attn_bwd_workspace_bytes(int B, int N, int Hq, int Hkv, int d) {
+  if (check_shape(B, N, Hq, Hkv, d) != ATTN_OK) return 0;
+  return attn::bwd_workspace_layout(B, N, Hq, Hkv, d).total;
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, void* workspace,
+             size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype, int causal,
+             float scale, void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULLPTR;
+  int st = check_shape(B, N, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return ATTN_ERR_ALIGN;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  const attn::BwdWorkspace ws = attn::bwd_workspace_layout(B, N, Hq, Hkv, d);
+  if (!workspace || workspace_bytes < ws.total) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+
+  attn::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.dq_acc_off);
+  a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.delta_off);
+  a.B = B;
+  a.N = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.group = Hq / Hkv;
+  a.scale = scale;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  hipError_t e = attn::launch_bwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0,
+                                  static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case ATTN_OK: return "success";
+    case ATTN_ERR_NULLPTR: return "a required pointer is NULL";
+    case ATTN_ERR_SHAPE: return "invalid shape (B, N, Hq, Hkv must be >= 1 and Hq a multiple of Hkv)";
+    case ATTN_ERR_HEADDIM: return "unsupported head dimension (expected 64, 128 or 256)";
+    case ATTN_ERR_DTYPE: return "unsupported dtype (expected ATTN_DTYPE_FP16 or ATTN_DTYPE_BF16)";
+    case ATTN_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case ATTN_ERR_SCALE: return "scale is not finite";
+    case ATTN_ERR_WORKSPACE: return "workspace is NULL or too small";
+    case ATTN_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
+    case ATTN_ERR_HIP: return "a HIP launch failed";
+    case ATTN_ERR_TOO_LARGE: return "sizes exceed the supported index range";
+    default: return "unknown status";
+  }
+}
+
+int attn_last_hip_error(void) { return g_last_hip_error; }
+
+const char* attn_version(void) { return "libattn 0.1.0 (gfx950)"; }
+
+}  // extern "C"

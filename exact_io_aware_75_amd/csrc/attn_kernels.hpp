@@ -1,0 +1,51 @@
+// Internal interface between the C-ABI host layer (attn_api.cpp) and the HIP
+// kernels.  Argument structs are passed by value to the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;  // [B, N, Hq, d]
+  const void* k;  // [B, N, Hkv, d]
+  const void* v;  // [B, N, Hkv, d]
+  void* o;        // [B, N, Hq, d]
+  float* lse;     // [B, Hq, N]
+  int B, N, Hq, Hkv;
+  int group;         // Hq / Hkv
+  int neg_scale;     // 1 if scale < 0 (folded into Q's sign)
+  float scale_log2;  // |scale| * log2(e)
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;  // [B, Hq, N]
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dq_acc;     // workspace: [B, N, Hq, d] fp32
+  float* delta;      // workspace: [B, Hq, N] fp32, rowsum(dO * O)
+  int B, N, Hq, Hkv;
+  int group;
+  float scale;       // signed softmax scale
+  float scale_log2;  // scale * log2(e)
+};
+
+// Workspace layout of the backward pass (offsets in bytes, 256-byte aligned).
+struct BwdWorkspace {
+  size_t dq_acc_off, dq_acc_bytes;
+  size_t delta_off, delta_bytes;
+  size_t total;
+};
+BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int Hkv, int d);
+
+hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream);
+
+}  // namespace attn

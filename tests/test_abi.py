@@ -1,0 +1,143 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/attn.h, and rejects invalid arguments with the documented
+status codes before launching anything."""
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_io_aware_75_amd import _lib
+
+    if not os.path.exists(_lib.library_path()):
+        from exact_io_aware_75_amd.build import build
+
+        build()
+    return _lib.load_library()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+
+
+def _status_codes():
+    text = open(HEADER).read()
+    return {k: int(v) for k, v in re.findall(r"\b(ATTN_(?:OK|ERR_[A-Z_]+))\s*=\s*(\d+)", text)}
+
+
+def test_header_declares_the_binding_exports():
+    from exact_io_aware_75_amd._lib import EXPORTS
+
+    assert _declared() == sorted(EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared():
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", lib._name], capture_output=True, text=True).stdout
+    for name in _declared():
+        assert re.search(rf"\bT {name}\b", out), name
+
+
+def test_strerror_and_version(lib):
+    codes = _status_codes()
+    assert codes["ATTN_OK"] == 0 and len(set(codes.values())) == len(codes)
+    for v in codes.values():
+        s = lib.attn_strerror(v).decode()
+        assert s and s != "unknown status"
+    assert lib.attn_strerror(12345).decode() == "unknown status"
+    assert b"gfx950" in lib.attn_version()
+    assert lib.attn_last_hip_error() == 0
+
+
+A = 0x10000  # fake, 16-byte aligned device addresses: never dereferenced on these paths
+
+
+def _fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, N=128, Hq=2, Hkv=2, d=64, dtype=1, causal=0, scale=0.125):
+    return lib.attn_fwd(q, k, v, o, lse, B, N, Hq, Hkv, d, dtype, causal, scale, None)
+
+
+def _bwd(lib, ws_bytes=None, ws=A, B=1, N=128, Hq=2, Hkv=2, d=64, dtype=1, scale=0.125, **ptrs):
+    p = dict(q=A, k=A, v=A, o=A, do=A, lse=A, dq=A, dk=A, dv=A)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = lib.attn_bwd_workspace_bytes(B, N, Hq, Hkv, d)
+    return lib.attn_bwd(p["q"], p["k"], p["v"], p["o"], p["do"], p["lse"], p["dq"], p["dk"], p["dv"],
+                        ws, ws_bytes, B, N, Hq, Hkv, d, dtype, 0, scale, None)
+
+
+def test_fwd_rejects_invalid_arguments(lib):
+    c = _status_codes()
+    assert _fwd(lib, q=None) == c["ATTN_ERR_NULLPTR"]
+    assert _fwd(lib, lse=None) == c["ATTN_ERR_NULLPTR"]
+    assert _fwd(lib, B=0) == c["ATTN_ERR_SHAPE"]
+    assert _fwd(lib, N=0) == c["ATTN_ERR_SHAPE"]
+    assert _fwd(lib, Hq=4, Hkv=3) == c["ATTN_ERR_SHAPE"]
+    assert _fwd(lib, Hkv=0) == c["ATTN_ERR_SHAPE"]
+    for d in (0, 32, 96, 512):
+        assert _fwd(lib, d=d) == c["ATTN_ERR_HEADDIM"]
+    assert _fwd(lib, dtype=2) == c["ATTN_ERR_DTYPE"]
+    assert _fwd(lib, v=A + 8) == c["ATTN_ERR_ALIGN"]
+    assert _fwd(lib, scale=math.nan) == c["ATTN_ERR_SCALE"]
+    assert _fwd(lib, scale=math.inf) == c["ATTN_ERR_SCALE"]
+    assert _fwd(lib, N=1 << 24, Hq=1, Hkv=1, d=128) == c["ATTN_ERR_TOO_LARGE"]
+
+
+def test_bwd_rejects_invalid_arguments(lib):
+    c = _status_codes()
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert _bwd(lib, **{name: None}) == c["ATTN_ERR_NULLPTR"], name
+    assert _bwd(lib, Hq=6, Hkv=4) == c["ATTN_ERR_SHAPE"]
+    assert _bwd(lib, d=80) == c["ATTN_ERR_HEADDIM"]
+    assert _bwd(lib, dtype=-1) == c["ATTN_ERR_DTYPE"]
+    assert _bwd(lib, dk=A + 4) == c["ATTN_ERR_ALIGN"]
+    assert _bwd(lib, scale=-math.inf) == c["ATTN_ERR_SCALE"]
+    need = lib.attn_bwd_workspace_bytes(1, 128, 2, 2, 64)
+    assert _bwd(lib, ws_bytes=need - 1) == c["ATTN_ERR_WORKSPACE"]
+    assert _bwd(lib, ws=None) == c["ATTN_ERR_WORKSPACE"]
+    assert _bwd(lib, ws=A + 2) == c["ATTN_ERR_ALIGN"]
+
+
+def test_workspace_is_linear_in_sequence_length(lib):
+    """Memory linear in N (FlashAttention-2 announcement, "具体实现": the tiled
+    method cuts memory from quadratic to linear in sequence length)."""
+    f = lambda n: lib.attn_bwd_workspace_bytes(2, n, 8, 2, 128)  # noqa: E731
+    sizes = [f(n) for n in (1024, 2048, 4096, 8192)]
+    assert all(s > 0 for s in sizes)
+    # exact affine form up to 256-byte alignment padding
+    assert abs((sizes[3] - sizes[2]) - 2 * (sizes[2] - sizes[1])) <= 512
+    assert sizes[3] <= 4.01 * sizes[1]
+    # at most an fp32 copy of dQ plus one fp32 per query row, plus padding
+    assert f(4096) <= 2 * 4096 * 8 * 128 * 4 + 2 * 8 * 4096 * 4 + 512
+    assert lib.attn_bwd_workspace_bytes(0, 16, 1, 1, 64) == 0
+    assert lib.attn_bwd_workspace_bytes(1, 16, 3, 2, 64) == 0
+
+
+def test_valid_call_without_gpu_reports_device_error():
+    """On a machine with no GPU a valid call must fail cleanly with
+    ATTN_ERR_DEVICE (run in a child process so the HIP runtime's probe of a
+    missing device cannot disturb this one)."""
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    code = (
+        "import ctypes,sys; sys.path.insert(0, %r)\n"
+        "from exact_io_aware_75_amd import _lib\n"
+        "lib=_lib.load_library()\n"
+        "print(lib.attn_fwd(%d,%d,%d,%d,%d,1,128,2,2,64,1,0,0.125,None))\n" % (ROOT, A, A, A, A, A)
+    )
+    r = subprocess.run(["python", "-c", code], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert int(r.stdout.strip().splitlines()[-1]) == _status_codes()["ATTN_ERR_DEVICE"]
