@@ -5,6 +5,7 @@ import sys
 
 import numpy as np
 
+from exact_io_aware_75_amd import configs
 from exact_io_aware_75_amd import inputs as gen
 
 # Tolerances stated for this path: max-abs error vs the fp64 oracle for
@@ -45,8 +46,42 @@ def run_fwd_bwd(x, dtype, causal, scale, device):
     return f(o), lse.cpu().numpy().astype(np.float64), f(dq), f(dk), f(dv)
 
 
+def half_ulp(ref, dtype):
+    """Half a unit in the last place of |ref| in the 16-bit output type: the
+    error of merely storing the exact result in that type (normal range)."""
+    mant = {"bf16": 7, "fp16": 10}[dtype]
+    mag = np.maximum(np.abs(ref), 2.0 ** -14)
+    return 0.5 * np.exp2(np.floor(np.log2(mag)) - mant)
+
+
+def excess(a, ref, tol, dtype):
+    """Largest (|a - ref| - allowed) over all elements, where allowed = tol +
+    half an output ulp of |ref|.  <= 0 means every element is within bounds.
+
+    The stated tolerances bound the computed value; the oracle is fp64 and
+    unrounded, so the comparison also allows the rounding of the result into
+    the 16-bit output type (which alone exceeds 1e-2 once |x| >= 4 in bf16).
+    """
+    if a.size == 0:
+        return 0.0
+    return float((np.abs(a - ref) - (tol + half_ulp(ref, dtype))).max())
+
+
 def max_err(a, ref):
     """(max abs error, |ref| at that element)."""
     diff = np.abs(a - ref)
     i = np.unravel_index(np.argmax(diff), diff.shape) if diff.size else ()
     return (float(diff[i]), float(np.abs(ref[i]))) if diff.size else (0.0, 0.0)
+
+
+def full_size_shapes():
+    """Every full-size workload: the hidden-size-2048 sweep (d = 64 and 128,
+    N = 512 .. 16384, causal and not), long sequences, GQA/MQA and d = 256."""
+    out = []
+    for d in (64, 128):
+        for n in configs.SWEEP_N:
+            for c in (False, True):
+                out.append(configs.hidden2048(d, n, c))
+    out += [configs.long_seq(32768), configs.long_seq(65536), configs.gqa(8), configs.gqa(1),
+            configs.wide_head()]
+    return out

@@ -1,0 +1,141 @@
+"""GPU parity of the backward pass (attn_bwd through the C ABI) against the
+CPU fp64 oracle, on seeded inputs.
+
+Small shapes: every element of dQ, dK, dV.  Full-size workloads (the launch
+configuration the benchmark times): dQ on sampled rows (computable row by
+row), dK/dV on a whole sampled K/V head where the oracle finishes in seconds,
+and at every size the gradient identities that hold exactly:
+sum_j dV_j = sum over the group's heads of sum_i dO_i, sum_j dK_j = 0 and,
+under a causal mask, dQ of row 0 = 0.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_io_aware_75_amd import inputs as gen
+from gpu_util import TOL_GRAD, TOL_LSE, TOL_O, excess, full_size_shapes, log, max_err, run_fwd_bwd
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_all(x, out, causal, scale, tag, dtype):
+    o, lse, dq, dk, dv = out
+    ro, rlse = oracle.attention_fwd(x["q"], x["k"], x["v"], causal, scale)
+    rdq, rdk, rdv = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], causal, scale)
+    errs = {n: max_err(a, r) for n, a, r in (("o", o, ro), ("lse", lse, rlse), ("dq", dq, rdq),
+                                             ("dk", dk, rdk), ("dv", dv, rdv))}
+    log(f"{tag}: " + "  ".join(f"{n}={e:.2e}(|ref| {m:.2f})" for n, (e, m) in errs.items()))
+    for t in (o, lse, dq, dk, dv):
+        assert np.isfinite(t).all()
+    assert excess(o, ro, TOL_O, dtype) <= 0, (tag, "o", errs["o"])
+    assert errs["lse"][0] <= TOL_LSE
+    for n, a_, r_ in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert excess(a_, r_, TOL_GRAD, dtype) <= 0, (tag, n, errs[n])
+
+
+SMALL = [
+    # b, n, hq, hkv, d, dtype
+    (1, 1, 1, 1, 64, "bf16"),
+    (2, 17, 2, 2, 64, "bf16"),
+    (1, 100, 4, 2, 128, "bf16"),
+    (1, 129, 2, 1, 128, "fp16"),
+    (1, 300, 2, 2, 256, "bf16"),
+    (1, 520, 4, 4, 64, "fp16"),
+    (1, 700, 2, 2, 128, "bf16"),
+    (1, 333, 8, 2, 256, "fp16"),
+    (2, 256, 4, 1, 128, "bf16"),
+    (1, 640, 2, 2, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("b,n,hq,hkv,d,dtype", SMALL)
+def test_small_shapes(gpu_device, b, n, hq, hkv, d, dtype, causal):
+    x = gen.make_inputs(b, n, hq, hkv, d, dtype, cfg_id=17, seed=n)
+    scale = 1.0 / np.sqrt(d)
+    out = run_fwd_bwd(x, dtype, causal, scale, gpu_device)
+    _check_all(x, out, causal, scale, f"b{b} n{n} hq{hq} hkv{hkv} d{d} {dtype} causal={causal}", dtype)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.1])
+def test_unusual_scales(gpu_device, scale):
+    x = gen.make_inputs(1, 150, 2, 1, 64, "bf16", cfg_id=18)
+    out = run_fwd_bwd(x, "bf16", True, scale, gpu_device)
+    _check_all(x, out, True, scale, f"scale={scale}", "bf16")
+
+
+def test_workspace_contents_are_ignored(gpu_device):
+    """A workspace full of garbage (NaNs) from a previous user gives the same result."""
+    import torch
+    import exact_io_aware_75_amd as ea
+
+    b, n, hq, hkv, d = 1, 200, 2, 2, 128
+    x = gen.make_inputs(b, n, hq, hkv, d, "bf16", cfg_id=19)
+    q, k, v, do = (gen.to_torch(x[t], "bf16", gpu_device) for t in ("q", "k", "v", "do"))
+    o, lse = ea.forward(q, k, v, causal=True)
+    ws = torch.full((ea.attn_bwd_workspace_bytes(b, n, hq, hkv, d),), 0xFF, dtype=torch.uint8,
+                    device=gpu_device)
+    dq, dk, dv = ea.backward(q, k, v, o, lse, do, causal=True, workspace=ws)
+    dq2, dk2, dv2 = ea.backward(q, k, v, o, lse, do, causal=True)
+    torch.cuda.synchronize()
+    for a_, b_ in ((dq, dq2), (dk, dk2), (dv, dv2)):
+        assert torch.isfinite(a_.float()).all()
+        assert (a_.float() - b_.float()).abs().max().item() <= 2 * 2 ** -7 * b_.float().abs().max().item()
+
+
+def _identities(s, x, dq, dk, dv):
+    rep = s.hq // s.hkv
+    dsum = x["do"].astype(np.float64).reshape(s.b, s.n, s.hkv, rep, s.d).sum(axis=(1, 3))
+    e_dv = np.abs(dv.sum(axis=1) - dsum).max()
+    e_dk = np.abs(dk.sum(axis=1)).max()
+    # sums of N rounded terms: allow the rounding of each dV/dK element (half ulp of
+    # the element's magnitude, <= 2^-8 relative in bf16) to accumulate like a random walk
+    tol_dv = 4 * np.sqrt(s.n) * 2 ** -8 * max(1.0, np.abs(dv).max())
+    tol_dk = 4 * np.sqrt(s.n) * 2 ** -8 * max(1.0, np.abs(dk).max())
+    log(f"  identities: |sum dV - sum dO|={e_dv:.3e} (tol {tol_dv:.2e})  |sum dK|={e_dk:.3e} (tol {tol_dk:.2e})")
+    assert e_dv <= tol_dv and e_dk <= tol_dk
+    if s.causal:
+        # row 0 attends only key 0, so P = 1 and dS = dP - D = 0 up to the fp32
+        # summation order of dP (MFMA) versus D (row sum): |dQ_0| ~ 1e-7
+        assert np.abs(dq[:, 0]).max() <= 1e-4
+
+
+@pytest.mark.parametrize("s", full_size_shapes(), ids=lambda s: f"{s.name}_n{s.n}_c{int(s.causal)}")
+def test_full_size(gpu_device, s):
+    x = gen.make_inputs(s.b, s.n, s.hq, s.hkv, s.d, s.dtype, cfg_id=s.cfg_id)
+    scale = 1.0 / np.sqrt(s.d)
+    log(f"full-size fwd+bwd {s}")
+    o, lse, dq, dk, dv = run_fwd_bwd(x, s.dtype, s.causal, scale, gpu_device)
+    for t in (o, lse, dq, dk, dv):
+        assert np.isfinite(t).all()
+    _identities(s, x, dq, dk, dv)
+    rng = np.random.default_rng(3 * s.n + s.d)
+    # dQ on sampled rows
+    worst = 0.0
+    over = -1.0
+    for _ in range(24):
+        bi, h, i = int(rng.integers(s.b)), int(rng.integers(s.hq)), int(rng.integers(s.n))
+        g = oracle.kv_head_of(h, s.hq, s.hkv)
+        rdq, _, _ = oracle.attention_head_bwd(x["q"][bi, :, h], x["k"][bi, :, g], x["v"][bi, :, g],
+                                              x["do"][bi, :, h], s.causal, scale, rows=[i])
+        worst = max(worst, float(np.abs(dq[bi, i, h] - rdq[0]).max()))
+        over = max(over, excess(dq[bi, i, h], rdq[0], TOL_GRAD, s.dtype))
+    log(f"  sampled dQ rows: max err {worst:.3e}")
+    assert over <= 0
+    # dK / dV of one whole K/V head where the oracle is quick
+    rep = s.hq // s.hkv
+    if s.n * s.n * rep <= 4096 * 4096 * 4:
+        bi, g = int(rng.integers(s.b)), int(rng.integers(s.hkv))
+        rdk = np.zeros((s.n, s.d))
+        rdv = np.zeros((s.n, s.d))
+        for h in range(g * rep, (g + 1) * rep):
+            _, a_, b_ = oracle.attention_head_bwd(x["q"][bi, :, h], x["k"][bi, :, g], x["v"][bi, :, g],
+                                                  x["do"][bi, :, h], s.causal, scale)
+            rdk += a_
+            rdv += b_
+        ek, _ = max_err(dk[bi, :, g], rdk)
+        ev, _ = max_err(dv[bi, :, g], rdv)
+        log(f"  K/V head (b={bi}, g={g}): max|ddK|={ek:.3e} max|ddV|={ev:.3e}")
+        assert excess(dk[bi, :, g], rdk, TOL_GRAD, s.dtype) <= 0
+        assert excess(dv[bi, :, g], rdv, TOL_GRAD, s.dtype) <= 0

@@ -14,18 +14,18 @@ import pytest
 import oracle
 from exact_io_aware_75_amd import configs
 from exact_io_aware_75_amd import inputs as gen
-from gpu_util import TOL_LSE, TOL_O, log, max_err, run_fwd
+from gpu_util import TOL_LSE, TOL_O, excess, full_size_shapes, log, max_err, run_fwd
 
 pytestmark = pytest.mark.gpu
 
 
-def _check_full(x, o, lse, causal, scale, tag):
+def _check_full(x, o, lse, causal, scale, tag, dtype="bf16"):
     ro, rlse = oracle.attention_fwd(x["q"], x["k"], x["v"], causal, scale)
     eo, mo = max_err(o, ro)
     el, ml = max_err(lse, rlse)
     log(f"{tag}: max|dO|={eo:.3e} (|ref|={mo:.2f})  max|dLSE|={el:.3e}")
     assert np.isfinite(o).all() and np.isfinite(lse).all()
-    assert eo <= TOL_O, (tag, eo, mo)
+    assert excess(o, ro, TOL_O, dtype) <= 0, (tag, eo, mo)
     assert el <= TOL_LSE, (tag, el, ml)
 
 
@@ -34,7 +34,7 @@ def test_small_fp16_config(gpu_device):
     s = configs.small_fp16()
     x = gen.make_inputs(s.b, s.n, s.hq, s.hkv, s.d, s.dtype, cfg_id=s.cfg_id, with_do=False)
     o, lse = run_fwd(x, s.dtype, s.causal, 1.0 / 8.0, gpu_device)
-    _check_full(x, o, lse, s.causal, 1.0 / 8.0, "small_fp16")
+    _check_full(x, o, lse, s.causal, 1.0 / 8.0, "small_fp16", "fp16")
 
 
 SMALL = [
@@ -58,7 +58,7 @@ def test_small_shapes(gpu_device, b, n, hq, hkv, d, dtype, causal):
     x = gen.make_inputs(b, n, hq, hkv, d, dtype, cfg_id=7, seed=n, with_do=False)
     scale = 1.0 / np.sqrt(d)
     o, lse = run_fwd(x, dtype, causal, scale, gpu_device)
-    _check_full(x, o, lse, causal, scale, f"b{b} n{n} hq{hq} hkv{hkv} d{d} {dtype} causal={causal}")
+    _check_full(x, o, lse, causal, scale, f"b{b} n{n} hq{hq} hkv{hkv} d{d} {dtype} causal={causal}", dtype)
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
@@ -106,17 +106,6 @@ def _sample_rows(s, rng, count=48):
     return picks
 
 
-def full_size_shapes():
-    out = []
-    for d in (64, 128):
-        for n in configs.SWEEP_N:
-            for c in (False, True):
-                out.append(configs.hidden2048(d, n, c))
-    out += [configs.long_seq(32768), configs.long_seq(65536), configs.gqa(8), configs.gqa(1),
-            configs.wide_head()]
-    return out
-
-
 @pytest.mark.parametrize("s", full_size_shapes(), ids=lambda s: f"{s.name}_n{s.n}_c{int(s.causal)}")
 def test_full_size_sampled_rows(gpu_device, s):
     x = gen.make_inputs(s.b, s.n, s.hq, s.hkv, s.d, s.dtype, cfg_id=s.cfg_id, with_do=False)
@@ -126,11 +115,13 @@ def test_full_size_sampled_rows(gpu_device, s):
     assert np.isfinite(o).all() and np.isfinite(lse).all()
     rng = np.random.default_rng(s.n + 17 * s.d)
     worst_o = worst_l = 0.0
+    over = -1.0
     for bi, h, i in _sample_rows(s, rng):
         g = oracle.kv_head_of(h, s.hq, s.hkv)
         ro, rl = oracle.attention_head_fwd(x["q"][bi, :, h], x["k"][bi, :, g], x["v"][bi, :, g],
                                            s.causal, scale, rows=[i])
         worst_o = max(worst_o, float(np.abs(o[bi, i, h] - ro[0]).max()))
+        over = max(over, excess(o[bi, i, h], ro[0], TOL_O, s.dtype))
         worst_l = max(worst_l, float(abs(lse[bi, h, i] - rl[0])))
     log(f"  sampled rows: max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
-    assert worst_o <= TOL_O and worst_l <= TOL_LSE
+    assert over <= 0 and worst_l <= TOL_LSE
