@@ -1,0 +1,389 @@
+"""Benchmark of the exact-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweep] [--no-cpu-baseline]
+
+A step is one pass of the whole path -- forward (attn_fwd) and backward
+(attn_bwd's three stages) -- over one batch of seeded synthetic input, once
+without and once with the causal mask, on the hidden-size-2048 attention layer
+with head dimension 128: B=4, N=4096, H=16, d=128, bf16, scale 1/sqrt(128).
+Throughput counts 4*B*H*N^2*d FLOPs per forward (halved when causal) and 2.5x
+that per backward.  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  Besides the throughput it carries
+  roofline      for the dominant kernel (the non-causal backward main kernel):
+                its algorithmic FLOPs / its mean duration from HIP events on its
+                own stream, against the dense bf16 MFMA peak; `traffic` is the HBM
+                bytes per launch measured with rocprofv3 counters for the current
+                kernel source (null when the source changed since);
+  cpu_baseline  the CPU fp64 oracle timed on a bounded sample of the same
+                workload on this host.
+--sweep also prints per-workload forward/backward TFLOP/s for every full-size
+configuration to stderr.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
+WORKLOAD = dict(name="hidden2048_d128", b=4, n=4096, h=16, d=128)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
+KERNEL_SOURCES = ("exact_io_aware_75_amd/csrc/attn_bwd.hip", "exact_io_aware_75_amd/csrc/attn_common.hpp")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def fwd_flops(b, n, h, d, causal):
+    f = 4.0 * b * h * n * n * d
+    return f / 2 if causal else f
+
+
+def load_traffic():
+    """HBM bytes per launch of the backward main kernel, if measured for this source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != kernel_source_hash():
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(seconds: float):
+    """Time the fp64 oracle on whole (batch, head) slices of the workload."""
+    import numpy as np
+
+    import oracle
+    from exact_io_aware_75_amd import inputs as gen
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        cores = os.cpu_count() or 1
+    w = WORKLOAD
+    n, d = w["n"], w["d"]
+    rng = np.random.default_rng(0)
+    flops = 0.0
+    slices = 0
+    elapsed = 0.0  # oracle time only; input generation is not counted
+    while elapsed < seconds:
+        causal = slices % 2 == 1
+        seed = int(rng.integers(1 << 30))
+        x = gen.make_inputs(1, n, 1, 1, d, "bf16", cfg_id=3, seed=seed)
+        q, k, v, do = (x[t][0, :, 0] for t in ("q", "k", "v", "do"))
+        scale = 1.0 / np.sqrt(d)
+        ts = time.perf_counter()
+        oracle.attention_head_fwd(q, k, v, causal, scale)
+        oracle.attention_head_bwd(q, k, v, do, causal, scale)
+        elapsed += time.perf_counter() - ts
+        flops += 3.5 * fwd_flops(1, n, 1, d, causal)
+        slices += 1
+    return {
+        "value": flops / elapsed / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{slices} (batch, head) slices of N={n}, d={d} (alternately non-causal and causal), "
+                  f"fwd+bwd in fp64, {elapsed:.1f} s; FLOPs counted as for the GPU",
+    }
+
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import exact_io_aware_75_amd as ea
+    from exact_io_aware_75_amd import inputs as gen
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = WORKLOAD
+    b, n, h, d = w["b"], w["n"], w["h"], w["d"]
+    scale = 1.0 / float(np.sqrt(d))
+    x = gen.make_inputs(b, n, h, h, d, "bf16", cfg_id=3)
+    q, k, v, do = (gen.to_torch(x[t], "bf16", dev) for t in ("q", "k", "v", "do"))
+    del x
+    o = torch.empty_like(q)
+    lse = torch.empty((b, h, n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(b, n, h, h, d), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    stages = ("attn_bwd_preprocess", "attn_bwd_main", "attn_bwd_convert_dq")
+    ops = []  # (label, callable)
+    for causal in (False, True):
+        tag = "causal" if causal else "noncausal"
+        ops.append((f"fwd_{tag}", lambda c=causal: ea.attn_fwd(q, k, v, o, lse, c, scale, stream)))
+        for st in stages:
+            ops.append((f"{st}_{tag}", lambda c=causal, s=st: ea.attn_bwd(
+                q, k, v, o, do, lse, dq, dk, dv, ws, c, scale, stream, stage=s)))
+
+    def step(events=None):
+        for i, (_, fn) in enumerate(ops):
+            if events is not None:
+                events[i].record(stream)
+            fn()
+        if events is not None:
+            events[len(ops)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    dur = {label: [] for label, _ in ops}
+    for s in range(args.steps):
+        for i, (label, _) in enumerate(ops):
+            dur[label].append(evs[s][i].elapsed_time(evs[s][i + 1]))
+    mean = {k_: float(np.mean(v_)) for k_, v_ in dur.items()}
+
+    flops_step = sum(3.5 * fwd_flops(b, n, h, d, c) for c in (False, True))
+    ms_per_step = wall / args.steps * 1e3
+    value = flops_step / (ms_per_step / 1e3) / 1e12
+    fwd_tf = {c: fwd_flops(b, n, h, d, c) / (mean[f"fwd_{'causal' if c else 'noncausal'}"] / 1e3) / 1e12
+              for c in (False, True)}
+    bwd_tf = {}
+    for c in (False, True):
+        tag = "causal" if c else "noncausal"
+        t_ms = sum(mean[f"{st}_{tag}"] for st in stages)
+        bwd_tf[c] = 2.5 * fwd_flops(b, n, h, d, c) / (t_ms / 1e3) / 1e12
+
+    main_ms = mean["attn_bwd_main_noncausal"]
+    achieved = 2.5 * fwd_flops(b, n, h, d, False) / (main_ms / 1e3) / 1e12
+    roofline = {
+        "bound": "mfma",
+        "kernel": "attn_bwd_main_kernel<bf16, d=128, non-causal>",
+        "achieved": round(achieved, 2),
+        "peak": PEAK_BF16_TFLOPS,
+        "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+        "traffic": load_traffic(),
+        "mean_ms": round(main_ms, 4),
+    }
+    line = {
+        "metric": "attention fwd/bwd TFLOP/s (bf16, causal/non, d=64/128) and % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded iid N(0,1), rounded to bf16)",
+        "config": {"workload": "attention layer, hidden size 2048, head dim 128: fwd+bwd, non-causal and causal",
+                   "B": b, "N": n, "H": h, "d": d, "scale": "1/sqrt(d)"},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": {"noncausal": round(fwd_tf[False], 2), "causal": round(fwd_tf[True], 2)},
+        "bwd_tflops": {"noncausal": round(bwd_tf[False], 2), "causal": round(bwd_tf[True], 2)},
+        "kernel_ms": {k_: round(v_, 4) for k_, v_ in mean.items()},
+        "roofline": roofline,
+    }
+    if args.sweep:
+        sweep()
+    if args.cpu_seconds > 0:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+def sweep():
+    """Per-configuration forward / backward throughput (HIP events, median of 10)."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_75_amd as ea
+    from exact_io_aware_75_amd import configs
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    shapes = []
+    for d in (64, 128):
+        for n in configs.SWEEP_N:
+            for c in (False, True):
+                shapes.append(configs.hidden2048(d, n, c))
+    shapes += [configs.long_seq(32768), configs.long_seq(65536), configs.gqa(8), configs.gqa(1),
+               configs.wide_head()]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    for s in shapes:
+        mk = lambda hh: torch.randn(s.b, s.n, hh, s.d, device=dev, generator=gen).to(torch.bfloat16)  # noqa: E731
+        q, k, v, do = mk(s.hq), mk(s.hkv), mk(s.hkv), mk(s.hq)
+        o, lse = torch.empty_like(q), torch.empty((s.b, s.hq, s.n), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(ea.attn_bwd_workspace_bytes(s.b, s.n, s.hq, s.hkv, s.d), dtype=torch.uint8, device=dev)
+        sc = 1.0 / float(np.sqrt(s.d))
+        res = {}
+        for name, fn in (("fwd", lambda: ea.attn_fwd(q, k, v, o, lse, s.causal, sc, stream)),
+                         ("bwd", lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, s.causal, sc, stream))):
+            for _ in range(3):
+                fn()
+            ts = []
+            for _ in range(10):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                e1.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            t = float(np.median(ts))
+            fl = s.fwd_flops() * (2.5 if name == "bwd" else 1.0)
+            res[name] = (t, fl / (t / 1e3) / 1e12)
+        print(f"sweep {s.name:16s} B={s.b:2d} N={s.n:6d} Hq={s.hq:2d} Hkv={s.hkv:2d} d={s.d:3d} causal={int(s.causal)}  "
+              f"fwd {res['fwd'][0]:8.3f} ms {res['fwd'][1]:7.1f} TFLOP/s ({100 * res['fwd'][1] / PEAK_BF16_TFLOPS:4.1f}%)  "
+              f"bwd {res['bwd'][0]:8.3f} ms {res['bwd'][1]:7.1f} TFLOP/s ({100 * res['bwd'][1] / PEAK_BF16_TFLOPS:4.1f}%)",
+              file=sys.stderr, flush=True)
+        del q, k, v, do, o, lse, dq, dk, dv, ws
+        torch.cuda.empty_cache()
+
+
+COPY_BYTES = 512 << 20  # calibration copy: reads and writes this many bytes per launch
+
+
+def copy_calibration():
+    """A plain device copy of known size, launched before the timed steps so the
+    same rocprofv3 counter run measures it: FETCH_SIZE / WRITE_SIZE of this
+    kernel against COPY_BYTES gives the scale from counter units to bytes."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)  # one elementwise kernel: reads and writes COPY_BYTES
+    torch.cuda.synchronize()
+
+
+def _read_csv(path):
+    import csv
+
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, cmd):
+    """Turn rocprofv3 CSV output into profiles/ summaries.
+
+    trace_dir: a --kernel-trace --stats run (kernel_stats.csv); fetch_dir /
+    write_dir: --pmc FETCH_SIZE and --pmc WRITE_SIZE runs (counter_collection.csv).
+    Writes profiles/bwd_main_kernel_stats.txt and profiles/bwd_main_traffic.json.
+    """
+    import glob
+
+    def find(d, pattern):
+        hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+        if not hits:
+            raise SystemExit(f"no {pattern} under {d}")
+        return hits[0]
+
+    stats = _read_csv(find(trace_dir, "*kernel_stats.csv"))
+    lines = [f"rocprofv3 --kernel-trace --stats summary (command: {cmd['trace']})", ""]
+    lines.append(f"{'kernel':100s} {'calls':>6s} {'avg_us':>10s} {'pct':>6s}")
+    for r in stats:
+        lines.append(f"{r['Name'][:100]:100s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['Percentage']):6.2f}")
+
+    def per_kernel(d, counter):
+        rows = _read_csv(find(d, "*counter_collection.csv"))
+        acc = {}
+        for r in rows:
+            if r.get("Counter_Name") != counter:
+                continue
+            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k_: sum(v_) / len(v_) for k_, v_ in acc.items()}
+
+    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
+    write = per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(table, key):
+        for name, val in table.items():
+            if key(name):
+                return name, val
+        raise SystemExit(f"kernel not found in counters: {list(table)[:5]}")
+
+    is_copy = lambda nm: "elementwise" in nm.lower() and "neg" in nm.lower()  # noqa: E731
+    is_main = lambda nm: "attn_bwd_main_kernel" in nm and (  # noqa: E731
+        "Bf16Tag, 128, false" in nm or "Bf16TagELi128ELb0E" in nm)
+    cname, cf = pick(fetch, is_copy)
+    _, cw = pick(write, is_copy)
+    mname, mf = pick(fetch, is_main)
+    _, mw = pick(write, is_main)
+    f_scale = COPY_BYTES / (cf * 1024.0)
+    w_scale = COPY_BYTES / (cw * 1024.0)
+    read_b = mf * 1024.0 * f_scale
+    write_b = mw * 1024.0 * w_scale
+    lines += ["", f"HBM traffic (commands: {cmd['fetch']} ; {cmd['write']})",
+              f"calibration kernel {cname[:80]}: FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB for "
+              f"{COPY_BYTES} B each -> scale {f_scale:.4f} / {w_scale:.4f}",
+              f"{mname[:100]}: FETCH_SIZE {mf:.0f} KiB, WRITE_SIZE {mw:.0f} KiB per dispatch -> "
+              f"{read_b / 1e6:.1f} MB read + {write_b / 1e6:.1f} MB written per launch"]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "bwd_main_kernel_stats.txt"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump({"kernel": mname, "source_sha256": kernel_source_hash(),
+                   "fetch_kib": mf, "write_kib": mw, "copy_fetch_kib": cf, "copy_write_kib": cw,
+                   "copy_bytes": COPY_BYTES, "read_bytes": read_b, "write_bytes": write_b,
+                   "bytes_per_launch": read_b + write_b, "commands": cmd}, f, indent=1)
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--sweep", action="store_true", help="also time every full-size configuration")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="CPU oracle baseline budget in seconds (0 disables it)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run a plain copy of known size first (for counter calibration)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/ summaries from rocprofv3 CSV output and exit")
+    ap.add_argument("--summarize-cmds", default="{}", help="JSON dict of the commands that made them")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(*args.summarize, json.loads(args.summarize_cmds))
+        return
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(the kernels shard trivially over batch and heads, but this build measures one GPU).",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.no_cpu_baseline:
+        args.cpu_seconds = 0.0
+    if args.copy_calibration:
+        copy_calibration()
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

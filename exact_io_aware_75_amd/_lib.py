@@ -20,8 +20,9 @@ ATTN_DTYPE_FP16 = 0
 ATTN_DTYPE_BF16 = 1
 
 # Entry points declared in include/attn.h (checked by the ABI test).
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_workspace_bytes", "attn_strerror",
-           "attn_last_hip_error", "attn_version")
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_main", "attn_bwd_convert_dq",
+           "attn_bwd_workspace_bytes", "attn_strerror", "attn_last_hip_error", "attn_version")
+BWD_STAGES = ("attn_bwd_preprocess", "attn_bwd_main", "attn_bwd_convert_dq")
 
 
 class AttnError(RuntimeError):
@@ -49,8 +50,10 @@ def load_library():
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     lib.attn_fwd.restype = i
-    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
-    lib.attn_bwd.restype = i
+    for name in ("attn_bwd",) + BWD_STAGES:
+        fn = getattr(lib, name)
+        fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
+        fn.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_strerror.argtypes = [i]
@@ -132,14 +135,18 @@ def attn_bwd_workspace_bytes(b: int, n: int, hq: int, hkv: int, d: int) -> int:
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
-             stream=None) -> None:
+             stream=None, stage: str = "attn_bwd") -> None:
     """Enqueue the backward pass into preallocated ``dq``, ``dk``, ``dv``.
 
     ``workspace`` is a uint8 device tensor of at least
-    ``attn_bwd_workspace_bytes(B, N, Hq, Hkv, d)`` bytes.
+    ``attn_bwd_workspace_bytes(B, N, Hq, Hkv, d)`` bytes.  ``stage`` selects
+    the whole pass ("attn_bwd") or one of its stages (``BWD_STAGES``), which
+    must then be enqueued in order.
     """
     import torch
 
+    if stage != "attn_bwd" and stage not in BWD_STAGES:
+        raise ValueError(f"unknown backward stage {stage!r}")
     lib = load_library()
     b, n, hq, hkv, d = _dims(q, k)
     for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, n, hkv, d), "k"),
@@ -151,11 +158,11 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: 
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                      _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, b, n, hq, hkv, d,
-                      _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
+    st = getattr(lib, stage)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                             _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, b, n, hq, hkv, d,
+                             _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
     if st != 0:
-        raise AttnError(st, "attn_bwd")
+        raise AttnError(st, stage)
 
 
 def _default_scale(d: int, scale):

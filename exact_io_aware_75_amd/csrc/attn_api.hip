@@ -112,10 +112,14 @@ size_t attn_bwd_workspace_bytes(int B, int N, int Hq, int Hkv, int d) {
   return attn::bwd_workspace_layout(B, N, Hq, Hkv, d).total;
 }
 
-int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
-             const float* lse, void* dq, void* dk, void* dv, void* workspace,
-             size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype, int causal,
-             float scale, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int bwd_common(int stages, const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
+               int causal, float scale, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULLPTR;
   int st = check_shape(B, N, Hq, Hkv, d);
   if (st != ATTN_OK) return st;
@@ -149,7 +153,7 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   a.group = Hq / Hkv;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
-  hipError_t e = attn::launch_bwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0,
+  hipError_t e = attn::launch_bwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0, stages,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
     g_last_hip_error = (int)e;
@@ -157,6 +161,27 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   }
   return ATTN_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+#define ATTN_BWD_ARGS                                                                       \
+  const void *q, const void *k, const void *v, const void *o, const void *dout,             \
+      const float *lse, void *dq, void *dk, void *dv, void *workspace,                      \
+      size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype, int causal,  \
+      float scale, void *stream
+#define ATTN_BWD_PASS                                                                       \
+  q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, N, Hq, Hkv, d, dtype,   \
+      causal, scale, stream
+
+int attn_bwd(ATTN_BWD_ARGS) { return bwd_common(7, ATTN_BWD_PASS); }
+int attn_bwd_preprocess(ATTN_BWD_ARGS) { return bwd_common(1, ATTN_BWD_PASS); }
+int attn_bwd_main(ATTN_BWD_ARGS) { return bwd_common(2, ATTN_BWD_PASS); }
+int attn_bwd_convert_dq(ATTN_BWD_ARGS) { return bwd_common(4, ATTN_BWD_PASS); }
+
+#undef ATTN_BWD_ARGS
+#undef ATTN_BWD_PASS
 
 const char* attn_strerror(int status) {
   switch (status) {

@@ -406,9 +406,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdArgs a, long long n
 }  // namespace
 
 template <typename Tag, int D, bool CAUSAL>
-hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   const long long rows = (long long)a.B * a.N * a.Hq;
-  {
+  if (stages & 1) {
     constexpr int ROWS = 256 / (D / 8);
     const long long grid = (rows + ROWS - 1) / ROWS;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -416,7 +416,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (stages & 2) {
     constexpr int BN = BwdCfg<D>::NW * 32;
     const long long grid = (long long)((a.N + BN - 1) / BN) * a.Hkv * a.B;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -425,7 +425,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  {
+  if (stages & 4) {
     const long long nchunks = rows * D / 8;
     const long long grid = (nchunks + 255) / 256;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -433,12 +433,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t stream) {
                        nchunks);
     return hipGetLastError();
   }
+  return hipSuccess;
 }
 
-hipError_t launch_bwd(const BwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream) {
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, int d, bool causal, int stages,
+                      hipStream_t stream) {
 #define ATTN_BWD_CASE(TAG, DD)                                                     \
-  if (d == DD) return causal ? launch_bwd_t<TAG, DD, true>(a, stream)             \
-                             : launch_bwd_t<TAG, DD, false>(a, stream);
+  if (d == DD) return causal ? launch_bwd_t<TAG, DD, true>(a, stages, stream)     \
+                             : launch_bwd_t<TAG, DD, false>(a, stages, stream);
   if (bf16) {
     ATTN_BWD_CASE(Bf16Tag, 64)
     ATTN_BWD_CASE(Bf16Tag, 128)

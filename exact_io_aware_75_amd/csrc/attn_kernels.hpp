@@ -46,6 +46,8 @@ struct BwdWorkspace {
 BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int Hkv, int d);
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream);
-hipError_t launch_bwd(const BwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream);
+// stage_mask: bit 0 = preprocess, bit 1 = main kernel, bit 2 = dQ conversion
+hipError_t launch_bwd(const BwdArgs& a, bool bf16, int d, bool causal, int stage_mask,
+                      hipStream_t stream);
 
 }  // namespace attn

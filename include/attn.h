@@ -109,6 +109,30 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
              int causal, float scale, void* stream);
 
+/*
+ * The three stages attn_bwd runs, exposed so a caller can schedule or time
+ * them separately.  Same arguments and validation as attn_bwd; they must be
+ * enqueued in this order on one stream with the same workspace, and together
+ * they are exactly attn_bwd:
+ *   attn_bwd_preprocess   D = rowsum(dout * o) per query row into the
+ *                         workspace, and the fp32 dQ accumulator set to zero;
+ *   attn_bwd_main         the recomputation loop: dk and dv written, dQ
+ *                         partial sums added into the accumulator;
+ *   attn_bwd_convert_dq   dq = scale * accumulator, rounded into `dtype`.
+ */
+int attn_bwd_preprocess(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int N, int Hq, int Hkv,
+                        int d, int dtype, int causal, float scale, void* stream);
+int attn_bwd_main(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
+                  int causal, float scale, void* stream);
+int attn_bwd_convert_dq(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        void* workspace, size_t workspace_bytes, int B, int N, int Hq, int Hkv,
+                        int d, int dtype, int causal, float scale, void* stream);
+
 /* Static, human-readable description of a status code. */
 const char* attn_strerror(int status);
 
