@@ -6,31 +6,39 @@
 //    result is folded into the output (FlashAttention-2 announcement, "具体实现"
 //    section; FlashAttention-1 news page, "FlashAttention" section).
 //  * Parallel over sequence length: one workgroup per (batch, query head,
-//    block of BM query rows), so the grid fills 256 CUs even for small
+//    block of 128 query rows), so the grid fills 256 CUs even for small
 //    batch * heads (announcement, "具体实现"; review, "Параллелизм").
 //  * Work split inside a workgroup: each 64-lane wavefront owns 32 query rows
 //    and all wavefronts share the K/V tiles, so wavefronts never exchange
 //    partial outputs (announcement, "具体实现": Q split across warps, K/V
 //    shared).
-//  * Online softmax with the rescale deferred: the running max only moves
+//  * Online softmax with the rescale deferred: the reference max only moves
 //    (and the accumulator is only rescaled) when a tile raises a row's max by
 //    more than 2^8 in the exp2 domain, and the single division by the row sum
 //    happens once in the epilogue -- fewer non-matmul operations without
 //    changing the output (announcement, "具体实现": the softmax trick
 //    rewritten to cut rescaling, bounds checks and causal masking).
-//  * Causal: key tiles wholly above the diagonal are never visited; only
+//  * Causal: key tiles wholly above the diagonal are never visited, and only
 //    tiles that cross the diagonal or the ragged end of the sequence run the
-//    element mask (review, "Алгоритм вычисления").
+//    element mask; the steady-state loop carries no mask code at all (review,
+//    "Алгоритм вычисления").
 //
-// CDNA4 mapping.  Scores are formed transposed, S^T = K Q^T, with
-// v_mfma_f32_32x32x16: the accumulator then holds one query per lane and 16
-// keys per register block, so row max / row sum are in-lane except one
-// exchange between lanes l and l ^ 32, and the probabilities are already the
-// B operand of O^T += V^T P^T.  V^T comes from the row-major V tile through
-// ds_read_b64_tr_b16.  Q stays in registers for the whole loop; K/V tiles are
-// double-buffered in LDS and the next tile's global loads are in flight while
-// the current one is consumed.  exp is v_exp_f32 (2^x) with log2(e) folded
-// into the score scale.
+// CDNA4 mapping.
+//  * Occupancy: two workgroups of four wavefronts per CU (two wavefronts per
+//    SIMD, <= 256 registers each), so one wavefront's softmax (VALU) runs
+//    while the other's matrix products (MFMA) run on the same SIMD.
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
+//    accumulator holds one query per lane and 16 keys per register block, so
+//    the row max / row sum are in-lane except one v_permlane32_swap between
+//    lanes l and l ^ 32, and the probabilities are already the B operand of
+//    O^T += V^T P^T.  V^T comes from the row-major V tile through
+//    ds_read_b64_tr_b16.  Q stays in registers for the whole loop.
+//  * K/V tiles go HBM -> LDS by global_load_lds_dwordx4 (no register staging),
+//    double-buffered: the next tile's loads are in flight while the current
+//    one is consumed.  The LDS tiles are unpadded and XOR-swizzled in 16-byte
+//    chunks so that both the 128-bit K reads and the transposed V reads are
+//    free of bank conflicts.
+//  * exp is v_exp_f32 (2^x) with log2(e) folded into the score scale.
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 
@@ -43,32 +51,45 @@ constexpr int FWD_WAVES = 4;    // 32 query rows per wavefront
 constexpr int FWD_THREADS = FWD_WAVES * 64;
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units: rescale only if the max grows > 2^8
 
-template <int D> struct FwdTile;
-template <> struct FwdTile<64> { static constexpr int BN = 128; };
-template <> struct FwdTile<128> { static constexpr int BN = 64; };
-template <> struct FwdTile<256> { static constexpr int BN = 32; };
+// Key-tile height per head dimension: every K or V tile is 16 KiB.
+template <int D> struct FwdTile { static constexpr int BN = 8192 / D; };
+
+// 16-byte-chunk swizzles of the LDS tiles (row r, logical chunk c is stored at
+// chunk c ^ swz(r)).  K is read 16 consecutive rows x one chunk at a time; V is
+// read by the transposed loads, 4 consecutive rows x 2 adjacent chunks at a time.
+template <int D> __device__ __forceinline__ int swz_k(int r) {
+  return D == 64 ? ((r >> 1) & 7) : (r & 15);
+}
+template <int D> __device__ __forceinline__ int swz_v(int r) {
+  return D == 64 ? 2 * ((r >> 1) & 3) : 2 * (r & 7);
+}
+
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// Wavefronts per SIMD the register budget is cut for: two for d <= 128; at
+// d = 256 the resident Q (64 registers) and O^T (128) leave too little for two.
+template <int D> struct FwdOcc { static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1; };
 
 template <typename Tag, int D, bool CAUSAL>
-__global__ void __launch_bounds__(FWD_THREADS)
+__global__ void __launch_bounds__(FWD_THREADS, FwdOcc<D>::WAVES_PER_SIMD)
 attn_fwd_kernel(FwdArgs a) {
   constexpr int BN = FwdTile<D>::BN;
-  constexpr int KSTR = D + 8;    // K tile row stride (elements): 16 B pad
-  constexpr int VSTR = D + 16;   // V tile row stride (elements): 32 B pad
-  constexpr int KT = BN * KSTR;
-  constexpr int VT = BN * VSTR;
-  constexpr int CPR = D / 8;                         // 16-byte chunks per row
-  constexpr int CPT = BN * CPR / FWD_THREADS;        // chunks per thread per tensor
-  constexpr int NKK = D / 16;                        // MFMA k-steps over d
-  constexpr int NSB = BN / 32;                       // 32-key sub-blocks per tile
-  constexpr int NDB = D / 32;                        // 32-wide d blocks of O
-  constexpr int NKS = BN / 16;                       // k-steps over keys in P V
-  static_assert(CPT >= 1 && BN * CPR % FWD_THREADS == 0, "tile/thread mismatch");
+  constexpr int CPR = D / 8;            // 16-byte chunks per row
+  constexpr int TILE = BN * D;          // elements per K or V tile (8192)
+  constexpr int LPT = TILE / 8 / FWD_THREADS;  // 16-byte loads per thread per tensor (4)
+  constexpr int NKK = D / 16;           // MFMA k-steps over d
+  constexpr int NSB = BN / 32;          // 32-key sub-blocks per tile
+  constexpr int NDB = D / 32;           // 32-wide d blocks of O
+  constexpr int NKS = BN / 16;          // k-steps over keys in P V
+  static_assert(TILE == 8192 && LPT == 4, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (KT + VT)];
+  // [buffer][K tile, V tile]
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: keep it scalar
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
@@ -82,14 +103,11 @@ attn_fwd_kernel(FwdArgs a) {
   const int h = bh - b * a.Hq;
   const int g = h / a.group;
 
-  const uint16_t* __restrict__ qp = (const uint16_t*)a.q;
-  const uint16_t* __restrict__ kp = (const uint16_t*)a.k;
-  const uint16_t* __restrict__ vp = (const uint16_t*)a.v;
   const size_t q_row = (size_t)a.Hq * D;   // elements between consecutive query rows
   const size_t kv_row = (size_t)a.Hkv * D;
-  const uint16_t* qbase = qp + ((size_t)b * a.N * a.Hq + h) * D;
-  const uint16_t* kbase = kp + ((size_t)b * a.N * a.Hkv + g) * D;
-  const uint16_t* vbase = vp + ((size_t)b * a.N * a.Hkv + g) * D;
+  const uint16_t* qbase = (const uint16_t*)a.q + ((size_t)b * a.N * a.Hq + h) * D;
+  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.N * a.Hkv + g) * D;
+  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.N * a.Hkv + g) * D;
 
   const int row0 = rb * FWD_BM;                 // first query row of the workgroup
   const int wrow0 = row0 + wave * 32;           // first query row of this wavefront
@@ -99,164 +117,214 @@ attn_fwd_kernel(FwdArgs a) {
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop ----
   frag8_t qf[NKK];
   {
-    const uint16_t* src = qbase + (size_t)qrow * q_row + 8 * half;
+    const uint16_t* src = qbase + (size_t)min(qrow, a.N - 1) * q_row + 8 * half;
+    const uint32_t flip = a.neg_scale ? 0x80008000u : 0u;  // a negative scale flips Q's sign
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      u32x4_t x = {0u, 0u, 0u, 0u};
-      if (qvalid) x = *(const u32x4_t*)(src + 16 * kk);
-      // a negative scale is folded into Q's sign so the score scale is >= 0
-      if (a.neg_scale) x ^= (u32x4_t){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      u32x4_t x = *(const u32x4_t*)(src + 16 * kk);
+      x ^= (u32x4_t){flip, flip, flip, flip};
       qf[kk] = __builtin_bit_cast(frag8_t, x);
     }
   }
   const float c = a.scale_log2;  // |scale| * log2(e)
 
-  // ---- key tiles this workgroup visits ----
+  // ---- key tiles: the workgroup's trip count and this wavefront's share ----
   const int ntiles_all = (a.N + BN - 1) / BN;
-  int ntiles = ntiles_all;
+  int ntiles = ntiles_all;   // tiles the workgroup streams through LDS
+  int nwave = ntiles_all;    // tiles this wavefront computes
+  int nfull = a.N / BN;      // leading tiles that need no element mask
   if (CAUSAL) {
-    const int last_row = min(row0 + FWD_BM, a.N) - 1;
-    ntiles = min(ntiles_all, last_row / BN + 1);
+    ntiles = min(ntiles_all, (min(row0 + FWD_BM, a.N) - 1) / BN + 1);
+    nwave = min(ntiles_all, (wrow0 + 31) / BN + 1);
+    nfull = min(nfull, (wrow0 + 1) / BN);
   }
 
-  // global -> register staging of one K/V tile (zeros past the sequence end)
-  u32x4_t kreg[CPT], vreg[CPT];
-  auto load_tile = [&](int j) {
+  // ---- HBM -> LDS tile loads: thread (wave, lane) fills chunk (4 i + wave) * 64 + lane ----
+  // of each tile for i = 0..3; its source row and logical chunk follow from the swizzle.
+  // Source offsets are 32-bit element offsets from the tile's first row (the
+  // host bounds N * H * d below 2^31).  Rows past the end of the sequence are
+  // redirected to the last row: any finite values do, since they are masked.
+  uint32_t ld_koff[LPT], ld_voff[LPT];
+  int ld_row[LPT];
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * FWD_THREADS;
-      const int r = cidx / CPR;
-      const int col = (cidx - r * CPR) * 8;
-      const int key = j * BN + r;
-      u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (key < a.N) {
-        kx = *(const u32x4_t*)(kbase + (size_t)key * kv_row + col);
-        vx = *(const u32x4_t*)(vbase + (size_t)key * kv_row + col);
+  for (int i = 0; i < LPT; ++i) {
+    const int q = (i * FWD_WAVES + wave) * 64 + lane;
+    const int r = q / CPR;
+    const int p = q % CPR;
+    ld_row[i] = r;
+    ld_koff[i] = (uint32_t)(r * (int)kv_row + (p ^ swz_k<D>(r)) * 8);
+    ld_voff[i] = (uint32_t)(r * (int)kv_row + (p ^ swz_v<D>(r)) * 8);
+  }
+  auto load_tile = [&](int j, int buf) {
+    uint16_t* kt = smem + buf * 2 * TILE;
+    uint16_t* vt = kt + TILE;
+    const size_t tile_off = (size_t)j * BN * kv_row;
+    const uint16_t* ksrc = kbase + tile_off;
+    const uint16_t* vsrc = vbase + tile_off;
+    if (j * BN + BN <= a.N) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int dst = (i * FWD_WAVES + wave) * 64 * 8;  // wave-uniform LDS element offset
+        __builtin_amdgcn_global_load_lds((gptr_t)(ksrc + ld_koff[i]), (lptr_t)(kt + dst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_t)(vsrc + ld_voff[i]), (lptr_t)(vt + dst), 16, 0, 0);
       }
-      kreg[i] = kx;
-      vreg[i] = vx;
-    }
-  };
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * (KT + VT);
-    uint16_t* vs = ks + KT;
+    } else {  // the tile runs past the sequence end
+      const int last = a.N - 1 - j * BN;  // last valid row of the tile
 #pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-      const int cidx = tid + i * FWD_THREADS;
-      const int r = cidx / CPR;
-      const int col = (cidx - r * CPR) * 8;
-      *(u32x4_t*)(ks + r * KSTR + col) = kreg[i];
-      *(u32x4_t*)(vs + r * VSTR + col) = vreg[i];
+      for (int i = 0; i < LPT; ++i) {
+        const uint32_t back = (uint32_t)(max(0, ld_row[i] - last) * (int)kv_row);
+        const int dst = (i * FWD_WAVES + wave) * 64 * 8;
+        __builtin_amdgcn_global_load_lds((gptr_t)(ksrc + (ld_koff[i] - back)), (lptr_t)(kt + dst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((gptr_t)(vsrc + (ld_voff[i] - back)), (lptr_t)(vt + dst), 16, 0, 0);
+      }
     }
   };
+
+  // ---- per-lane LDS read offsets (elements, within one tile) ----
+  // K (A operand of S^T): row 32 sb + l32, logical chunk 2 kk + half.
+  int k_rd[NKK];
+  {
+    const int x = swz_k<D>(l32) ^ half;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) k_rd[kk] = l32 * D + ((2 * kk) ^ x) * 8;
+  }
+  // V^T (A operand of O^T += V^T P^T) by transposed reads: row 16 ks + 8 hi + 4 half + gi / 4,
+  // element 32 db + 16 (grp & 1) + 4 (gi & 3), i.e. logical chunk 4 db + cl.
+  int v_rd[NDB];
+  {
+    const int grp = lane >> 4;
+    const int gi = lane & 15;
+    const int r = 4 * half + (gi >> 2);
+    const int cl = 2 * (grp & 1) + ((gi & 3) >> 1);
+    const int x = swz_v<D>(r) ^ cl;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) v_rd[db] = r * D + ((4 * db) ^ x) * 8 + 4 * (gi & 1);
+  }
 
   f32x16_t oacc[NDB];
 #pragma unroll
   for (int i = 0; i < NDB; ++i) oacc[i] = (f32x16_t){};
   float m_ref = -INFINITY;  // running max (exp2 domain) the accumulator is scaled to
-  float lsum = 0.f;         // this lane's partial row sum (keys of its half)
+  float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial row sums (keys of its half)
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < ntiles; ++j) {
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1);
-    const int kbase_j = j * BN;
-    const bool wave_active = !CAUSAL || kbase_j <= wrow0 + 31;
-    if (wave_active) {
-      const uint16_t* ks = smem + buf * (KT + VT);
-      const uint16_t* vs = ks + KT;
-      // S^T = K Q^T for this wavefront's 32 queries
-      f32x16_t s[NSB];
+  auto do_tile = [&](int j, const uint16_t* ks, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const uint16_t* vs = ks + TILE;
+    const int key0 = j * BN;
+    // S^T = K Q^T for this wavefront's 32 queries
+    f32x16_t s[NSB];
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-        f32x16_t acc = {};
-        const uint16_t* krow = ks + (32 * sb + l32) * KSTR + 8 * half;
+    for (int sb = 0; sb < NSB; ++sb) {
+      f32x16_t acc = {};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          frag8_t kf = *(const frag8_t*)(krow + 16 * kk);
-          acc = mfma32(Tag{}, kf, qf[kk], acc);
-        }
-        s[sb] = acc;
+      for (int kk = 0; kk < NKK; ++kk) {
+        frag8_t kf = *(const frag8_t*)(ks + 32 * sb * D + k_rd[kk]);
+        acc = mfma32(Tag{}, kf, qf[kk], acc);
       }
-      // element mask only on tiles that cross the diagonal or the sequence end
-      const bool need_mask = (kbase_j + BN > a.N) || (CAUSAL && kbase_j + BN - 1 > wrow0);
-      float mx = -INFINITY;
-      if (need_mask) {
+      s[sb] = acc;
+    }
+    if (MASK) {
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb)
+      for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kbase_j + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = key < a.N && (!CAUSAL || key <= qrow);
-            mx = fmaxf(mx, ok ? s[sb][r] : -INFINITY);
+        for (int r = 0; r < 16; ++r) {
+          const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool ok = key < a.N && (!CAUSAL || key <= qrow);
+          s[sb][r] = ok ? s[sb][r] : -INFINITY;
+        }
+    }
+    // row max: four independent v_max3 chains, then one exchange between the halves
+    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        mx4[(r >> 1) & 3] = fmaxf(mx4[(r >> 1) & 3], fmaxf(s[sb][r], s[sb][r + 1]));
+    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                       __builtin_bit_cast(uint32_t, mx), false, false);
+      mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+    }
+    const float mxs = mx * c;
+    // deferred rescale: move the reference max only when it grows by > 2^8
+    if (__builtin_amdgcn_ballot_w64(mxs > m_ref + RESCALE_THRESHOLD) != 0) {
+      const float m_new = fmaxf(m_ref, mxs);
+      const float alpha = fast_exp2(m_ref - m_new);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) lsum[t] *= alpha;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+      m_ref = m_new;
+    }
+    // P = 2^(s*c - m_ref), rounded to 16 bits: the B operand of O^T += V^T P^T
+    const float nm = -m_ref;
+    frag8_t pf[NKS];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 8 * hh + 2 * t;
+          float p0 = fast_exp2(__builtin_fmaf(s[sb][r], c, nm));
+          float p1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], c, nm));
+          if (MASK) {  // exp2(-inf * 0) would be NaN when scale == 0
+            p0 = s[sb][r] == -INFINITY ? 0.f : p0;
+            p1 = s[sb][r + 1] == -INFINITY ? 0.f : p1;
           }
-      } else {
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-      }
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float mxs = mx * c;  // NaN only if the row is fully masked and c == 0
-      // deferred rescale: move the reference max only when it grows by > 2^8
-      const bool grow = mxs > m_ref + RESCALE_THRESHOLD;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float m_new = fmaxf(m_ref, mxs);
-        const float alpha = fast_exp2(m_ref - m_new);
-        lsum *= alpha;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-        m_ref = m_new;
-      }
-      // P = 2^(s*c - m_ref), rounded to 16 bits: the B operand of O^T += V^T P^T
-      frag8_t pf[NKS];
-#pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) {
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint32_t w[4];
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int r = 8 * hh + 2 * t;
-            float p0 = fast_exp2(s[sb][r] * c - m_ref);
-            float p1 = fast_exp2(s[sb][r + 1] * c - m_ref);
-            if (need_mask) {
-              const int key0 = kbase_j + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-              if (!(key0 < a.N && (!CAUSAL || key0 <= qrow))) p0 = 0.f;
-              if (!(key0 + 1 < a.N && (!CAUSAL || key0 + 1 <= qrow))) p1 = 0.f;
-            }
-            w[t] = pack2(Tag{}, p0, p1);
-            lsum += p0 + p1;  // fp32 row sum: LSE must not carry 16-bit rounding
-          }
-          u32x4_t wv = {w[0], w[1], w[2], w[3]};
-          pf[2 * sb + hh] = __builtin_bit_cast(frag8_t, wv);
+          w[t] = pack2(Tag{}, p0, p1);
+          lsum[t] += p0 + p1;  // fp32 row sum: LSE must not carry 16-bit rounding
         }
-      }
-      // O^T += V^T P^T : A operand V^T via transposed LDS reads
-      const int grp = lane >> 4;         // 16-lane group
-      const int gi = lane & 15;
-      const uint16_t* vrd = vs + (4 * half + (gi >> 2)) * VSTR + 16 * (grp & 1) + 4 * (gi & 3);
-#pragma unroll
-      for (int ksb = 0; ksb < NKS; ++ksb) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const uint16_t* p = vrd + (16 * ksb) * VSTR + 32 * db;
-          s16x4_t lo = lds_read_tr(p);
-          s16x4_t hi = lds_read_tr(p + 8 * VSTR);
-          frag8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          oacc[db] = mfma32(Tag{}, vf, pf[ksb], oacc[db]);
-        }
+        u32x4_t wv = {w[0], w[1], w[2], w[3]};
+        pf[2 * sb + hh] = __builtin_bit_cast(frag8_t, wv);
       }
     }
-    if (j + 1 < ntiles) store_tile(buf ^ 1);
+    // O^T += V^T P^T : A operand V^T via transposed LDS reads
+#pragma unroll
+    for (int ksb = 0; ksb < NKS; ++ksb) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const uint16_t* p = vs + 16 * ksb * D + v_rd[db];
+        s16x4_t lo = lds_read_tr(p);
+        s16x4_t hi = lds_read_tr(p + 8 * D);
+        frag8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        oacc[db] = mfma32(Tag{}, vf, pf[ksb], oacc[db]);
+      }
+    }
+  };
+
+  load_tile(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  // Two loops with one barrier per tile each: every wavefront passes exactly
+  // `ntiles` barriers, whichever loop it spends them in.
+  int j = 0;
+  for (; j < nfull; ++j) {  // steady state: no element mask
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
+    do_tile(j, smem + buf * 2 * TILE, std::false_type{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  for (; j < ntiles; ++j) {  // diagonal / ragged tiles, then tiles only other wavefronts need
+    const int buf = j & 1;
+    if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
+    if (j < nwave) do_tile(j, smem + buf * 2 * TILE, std::true_type{});
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
   // ---- epilogue: one division per row, LSE in natural log ----
-  const float ltot = lsum + wave_xor32(lsum);
+  float ltot;
+  {
+    const float ls = (lsum[0] + lsum[1]) + (lsum[2] + lsum[3]);
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, ls),
+                                                     __builtin_bit_cast(uint32_t, ls), false, false);
+    ltot = __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
+  }
   if (qvalid) {
     const float inv = 1.0f / ltot;
     uint16_t* orow = (uint16_t*)a.o + ((size_t)b * a.N * a.Hq + h) * D + (size_t)qrow * q_row;
