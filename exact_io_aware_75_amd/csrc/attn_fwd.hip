@@ -55,13 +55,16 @@ constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units: rescale only if the ma
 template <int D> struct FwdTile { static constexpr int BN = 8192 / D; };
 
 // 16-byte-chunk swizzles of the LDS tiles (row r, logical chunk c is stored at
-// chunk c ^ swz(r)).  K is read 16 consecutive rows x one chunk at a time; V is
-// read by the transposed loads, 4 consecutive rows x 2 adjacent chunks at a time.
+// chunk c ^ swz(r)); LDS has 64 four-byte banks, i.e. 16 chunk-wide bank groups.
+// K: a 128-bit read serves 16 lanes per cycle, here 16 consecutive rows at one
+// logical chunk, so the 16 rows must land in 16 different bank groups.
+// V: a transposed 64-bit read serves 32 lanes per cycle, here 4 consecutive
+// rows x 4 adjacent chunks, so each of the 4 rows must own 4 bank groups.
 template <int D> __device__ __forceinline__ int swz_k(int r) {
   return D == 64 ? ((r >> 1) & 7) : (r & 15);
 }
 template <int D> __device__ __forceinline__ int swz_v(int r) {
-  return D == 64 ? 2 * ((r >> 1) & 3) : 2 * (r & 7);
+  return D == 64 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
 }
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
@@ -84,8 +87,10 @@ attn_fwd_kernel(FwdArgs a) {
   constexpr int NKS = BN / 16;          // k-steps over keys in P V
   static_assert(TILE == 8192 && LPT == 4, "tile shape");
 
-  // [buffer][K tile, V tile]
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[2 * 2 * TILE];
+  // Two LDS buffers of [K tile, V tile], as separate objects so the compiler can
+  // tell that the loads in flight into one never alias reads of the other.
+  __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -141,26 +146,24 @@ attn_fwd_kernel(FwdArgs a) {
 
   // ---- HBM -> LDS tile loads: thread (wave, lane) fills chunk (4 i + wave) * 64 + lane ----
   // of each tile for i = 0..3; its source row and logical chunk follow from the swizzle.
-  // Source offsets are 32-bit element offsets from the tile's first row (the
-  // host bounds N * H * d below 2^31).  Rows past the end of the sequence are
-  // redirected to the last row: any finite values do, since they are masked.
+  // Source offsets are 32-bit byte offsets from the tile's first row (the host
+  // bounds N * H * d below 2^31 elements), so each load is a scalar base plus
+  // one vector offset.  Rows past the end of the sequence are redirected to
+  // the last row: any finite values do, since they are masked.
   uint32_t ld_koff[LPT], ld_voff[LPT];
-  int ld_row[LPT];
 #pragma unroll
   for (int i = 0; i < LPT; ++i) {
     const int q = (i * FWD_WAVES + wave) * 64 + lane;
     const int r = q / CPR;
     const int p = q % CPR;
-    ld_row[i] = r;
-    ld_koff[i] = (uint32_t)(r * (int)kv_row + (p ^ swz_k<D>(r)) * 8);
-    ld_voff[i] = (uint32_t)(r * (int)kv_row + (p ^ swz_v<D>(r)) * 8);
+    ld_koff[i] = (uint32_t)(2 * (r * (int)kv_row + (p ^ swz_k<D>(r)) * 8));
+    ld_voff[i] = (uint32_t)(2 * (r * (int)kv_row + (p ^ swz_v<D>(r)) * 8));
   }
-  auto load_tile = [&](int j, int buf) {
-    uint16_t* kt = smem + buf * 2 * TILE;
+  auto load_tile = [&](int j, uint16_t* kt) {
     uint16_t* vt = kt + TILE;
     const size_t tile_off = (size_t)j * BN * kv_row;
-    const uint16_t* ksrc = kbase + tile_off;
-    const uint16_t* vsrc = vbase + tile_off;
+    const char* ksrc = (const char*)(kbase + tile_off);
+    const char* vsrc = (const char*)(vbase + tile_off);
     if (j * BN + BN <= a.N) {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
@@ -172,7 +175,8 @@ attn_fwd_kernel(FwdArgs a) {
       const int last = a.N - 1 - j * BN;  // last valid row of the tile
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
-        const uint32_t back = (uint32_t)(max(0, ld_row[i] - last) * (int)kv_row);
+        const int r = ((i * FWD_WAVES + wave) * 64 + lane) / CPR;
+        const uint32_t back = (uint32_t)(2 * max(0, r - last) * (int)kv_row);
         const int dst = (i * FWD_WAVES + wave) * 64 * 8;
         __builtin_amdgcn_global_load_lds((gptr_t)(ksrc + (ld_koff[i] - back)), (lptr_t)(kt + dst), 16, 0, 0);
         __builtin_amdgcn_global_load_lds((gptr_t)(vsrc + (ld_voff[i] - back)), (lptr_t)(vt + dst), 16, 0, 0);
@@ -211,17 +215,32 @@ attn_fwd_kernel(FwdArgs a) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const uint16_t* vs = ks + TILE;
     const int key0 = j * BN;
-    // S^T = K Q^T for this wavefront's 32 queries
+    // S^T = K Q^T for this wavefront's 32 queries.  The NSB accumulator chains
+    // advance together one k-step at a time, and the K fragments are read
+    // PF k-steps ahead, so no product waits on its own LDS read.
     f32x16_t s[NSB];
+    {
+      constexpr int PF = 2;
+      frag8_t kf[PF + 1][NSB];
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-      f32x16_t acc = {};
+      for (int sb = 0; sb < NSB; ++sb) s[sb] = (f32x16_t){};
+#pragma unroll
+      for (int kk = 0; kk < PF && kk < NKK; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) kf[kk][sb] = *(const frag8_t*)(ks + 32 * sb * D + k_rd[kk]);
+      __builtin_amdgcn_sched_group_barrier(0x100, PF * NSB, 0);  // DS reads
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        frag8_t kf = *(const frag8_t*)(ks + 32 * sb * D + k_rd[kk]);
-        acc = mfma32(Tag{}, kf, qf[kk], acc);
+        if (kk + PF < NKK) {
+#pragma unroll
+          for (int sb = 0; sb < NSB; ++sb)
+            kf[(kk + PF) % (PF + 1)][sb] = *(const frag8_t*)(ks + 32 * sb * D + k_rd[kk + PF]);
+        }
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb) s[sb] = mfma32(Tag{}, kf[kk % (PF + 1)][sb], qf[kk], s[sb]);
+        if (kk + PF < NKK) __builtin_amdgcn_sched_group_barrier(0x100, NSB, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, NSB, 0);                     // MFMA
       }
-      s[sb] = acc;
     }
     if (MASK) {
 #pragma unroll
@@ -295,24 +314,35 @@ attn_fwd_kernel(FwdArgs a) {
     }
   };
 
-  load_tile(0, 0);
+  uint16_t* const buf0 = smem0;
+  uint16_t* const buf1 = smem1;
+  load_tile(0, buf0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
-  // Two loops with one barrier per tile each: every wavefront passes exactly
-  // `ntiles` barriers, whichever loop it spends them in.
-  int j = 0;
-  for (; j < nfull; ++j) {  // steady state: no element mask
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
-    do_tile(j, smem + buf * 2 * TILE, std::false_type{});
+  // One barrier per tile: every wavefront passes exactly `ntiles` barriers,
+  // whichever loop it spends them in.  Tile j lives in buffer j & 1; the
+  // steady-state loop takes tiles in pairs so both buffer offsets are constants.
+  auto step = [&](int j, uint16_t* cur, uint16_t* nxt, auto mask_tag) {
+    if (j + 1 < ntiles) load_tile(j + 1, nxt);
+    do_tile(j, cur, mask_tag);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+  int j = 0;
+  for (; j + 1 < nfull; j += 2) {  // steady state: no element mask
+    step(j, buf0, buf1, std::false_type{});
+    step(j + 1, buf1, buf0, std::false_type{});
+  }
+  if (j < nfull) {
+    step(j, buf0, buf1, std::false_type{});
+    ++j;
   }
   for (; j < ntiles; ++j) {  // diagonal / ragged tiles, then tiles only other wavefronts need
-    const int buf = j & 1;
-    if (j + 1 < ntiles) load_tile(j + 1, buf ^ 1);
-    if (j < nwave) do_tile(j, smem + buf * 2 * TILE, std::true_type{});
+    uint16_t* cur = (j & 1) ? buf1 : buf0;
+    uint16_t* nxt = (j & 1) ? buf0 : buf1;
+    if (j + 1 < ntiles) load_tile(j + 1, nxt);
+    if (j < nwave) do_tile(j, cur, std::true_type{});
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
