@@ -126,7 +126,7 @@ def run(args):
     ws = torch.empty(ea.attn_bwd_workspace_bytes(b, n, h, h, d), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
-    stages = ("attn_bwd_preprocess", "attn_bwd_main", "attn_bwd_convert_dq")
+    stages = ("attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq")
     ops = []  # (label, callable)
     for causal in (False, True):
         tag = "causal" if causal else "noncausal"
@@ -172,11 +172,13 @@ def run(args):
         t_ms = sum(mean[f"{st}_{tag}"] for st in stages)
         bwd_tf[c] = 2.5 * fwd_flops(b, n, h, d, c) / (t_ms / 1e3) / 1e12
 
-    main_ms = mean["attn_bwd_main_noncausal"]
-    achieved = 2.5 * fwd_flops(b, n, h, d, False) / (main_ms / 1e3) / 1e12
+    # Dominant kernel: the non-causal dK/dV kernel.  Its algorithmic work is
+    # four N x N x d products per (batch, head): S, dP, dV, dK = 8 B H N^2 d FLOP.
+    main_ms = mean["attn_bwd_dkdv_noncausal"]
+    achieved = 8.0 * b * h * n * n * d / (main_ms / 1e3) / 1e12
     roofline = {
         "bound": "mfma",
-        "kernel": "attn_bwd_main_kernel<bf16, d=128, non-causal>",
+        "kernel": "attn_bwd_dkdv_kernel<bf16, d=128, non-causal>",
         "achieved": round(achieved, 2),
         "peak": PEAK_BF16_TFLOPS,
         "unit": "TFLOP/s",

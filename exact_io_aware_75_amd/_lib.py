@@ -20,9 +20,9 @@ ATTN_DTYPE_FP16 = 0
 ATTN_DTYPE_BF16 = 1
 
 # Entry points declared in include/attn.h (checked by the ABI test).
-EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_main", "attn_bwd_convert_dq",
+EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
            "attn_bwd_workspace_bytes", "attn_strerror", "attn_last_hip_error", "attn_version")
-BWD_STAGES = ("attn_bwd_preprocess", "attn_bwd_main", "attn_bwd_convert_dq")
+BWD_STAGES = ("attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq")
 
 
 class AttnError(RuntimeError):

@@ -61,9 +61,8 @@ namespace attn {
 
 BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int /*Hkv*/, int d) {
   BwdWorkspace w;
-  w.dq_acc_off = 0;
-  w.dq_acc_bytes = (size_t)B * N * Hq * d * sizeof(float);
-  w.delta_off = align256(w.dq_acc_bytes);
+  (void)d;
+  w.delta_off = 0;
   w.delta_bytes = (size_t)B * Hq * N * sizeof(float);
   w.total = align256(w.delta_off + w.delta_bytes);
   return w;
@@ -144,7 +143,6 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;
-  a.dq_acc = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.dq_acc_off);
   a.delta = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.delta_off);
   a.B = B;
   a.N = N;
@@ -177,8 +175,8 @@ extern "C" {
 
 int attn_bwd(ATTN_BWD_ARGS) { return bwd_common(7, ATTN_BWD_PASS); }
 int attn_bwd_preprocess(ATTN_BWD_ARGS) { return bwd_common(1, ATTN_BWD_PASS); }
-int attn_bwd_main(ATTN_BWD_ARGS) { return bwd_common(2, ATTN_BWD_PASS); }
-int attn_bwd_convert_dq(ATTN_BWD_ARGS) { return bwd_common(4, ATTN_BWD_PASS); }
+int attn_bwd_dkdv(ATTN_BWD_ARGS) { return bwd_common(2, ATTN_BWD_PASS); }
+int attn_bwd_dq(ATTN_BWD_ARGS) { return bwd_common(4, ATTN_BWD_PASS); }
 
 #undef ATTN_BWD_ARGS
 #undef ATTN_BWD_PASS

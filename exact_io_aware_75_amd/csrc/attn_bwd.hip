@@ -8,22 +8,36 @@
 //     dK = scale * dS^T Q,  dQ = scale * dS K
 //
 // Three launches on the caller's stream:
-//  1. bwd_pre:  D = rowsum(dO * O) per query row (fp32) and dQacc = 0.
-//  2. bwd_main: one workgroup per (batch, K/V head, block of keys) -- parallel
-//     over the key (column) dimension, as the pages describe for the backward
-//     pass (FlashAttention-2 review, "Параллелизм").  Each 64-lane wavefront
-//     owns 32 keys; dK and dV stay in registers for the whole loop over the
-//     query heads of the GQA group and the query tiles (causal: only tiles
-//     at or below the diagonal).  dQ partials go to an fp32 accumulator with
-//     atomic adds.
-//  3. bwd_dq:   dQ = scale * dQacc rounded to the input dtype.
+//  1. bwd_pre:  D = rowsum(dO * O) per query row (fp32).
+//  2. bwd_dkdv: one workgroup per (batch, K/V head, block of 128 keys) --
+//     parallel over the key (column) dimension, as the pages describe for
+//     the backward pass (FlashAttention-2 review, "Параллелизм").  Each
+//     wavefront owns 32 keys; dK and dV stay in registers through the loop
+//     over the query heads of the GQA group and the query tiles (causal: only
+//     tiles at or below the diagonal).  Products: S, dP, dV, dK.
+//  3. bwd_dq:   one workgroup per (batch, query head, block of 128 queries) --
+//     parallel over rows like the forward pass.  Each wavefront owns 32
+//     queries and recomputes S and dP for them, then dQ += dS K.  Products:
+//     S, dP, dQ.
 //
-// CDNA4 mapping (v_mfma_f32_32x32x16, 64-lane wavefronts).  Scores are formed
-// as S = Q K^T with the key index on the lane, so P and dS come out of the
-// accumulators already laid out as the B operands of dV^T += dO^T P and
-// dK^T += Q^T dS; dO^T and Q^T are read from the row-major LDS tiles with
-// ds_read_b64_tr_b16.  dS is staged once through LDS (as 16-bit values) for
-// dQ = dS K, whose K operand is again a transposed LDS read.
+// Splitting dQ off costs two extra products (seven instead of five) but
+// replaces the fp32 atomic accumulation of dQ partials, which on this 8-XCD
+// part run past the per-XCD L2 (4+ GB of memory-side atomics per launch at
+// N = 4k), and the cross-wavefront staging of dS; the result is also
+// deterministic.
+//
+// CDNA4 mapping (v_mfma_f32_32x32x16, 64-lane wavefronts, two wavefronts per
+// SIMD for d <= 128).  Tiles move HBM -> LDS by global_load_lds_dwordx4 into
+// unpadded tiles swizzled in 16-byte chunks; the swizzle is free of bank
+// conflicts both for 128-bit row reads (16 rows x one chunk per cycle) and
+// for ds_read_b64_tr_b16 transposed reads (4 rows x 4 chunks per cycle),
+// because every tile here is read both ways.
+//  * dK/dV: S = Q K^T and dP = dO V^T with the key on the lane, so P and dS
+//    are directly the B operands of dV^T += dO^T P and dK^T += Q^T dS; dO^T
+//    and Q^T are transposed reads of the Q / dO tiles.
+//  * dQ: S^T = K Q^T and dP^T = V dO^T with the query on the lane (LSE and D
+//    are per lane), so dS^T is directly the B operand of dQ^T += K^T dS^T;
+//    K^T is a transposed read of the K tile.
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 
@@ -31,8 +45,108 @@ namespace attn {
 
 namespace {
 
+typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef __attribute__((address_space(3))) void* lptr_t;
+
+// 16-byte-chunk swizzle (row r, logical chunk c stored at chunk c ^ swz(r));
+// 64 four-byte banks = 16 chunk-wide bank groups.  A 128-bit read serves 16
+// lanes per cycle (here 16 consecutive rows at one logical chunk: swz must
+// be a bijection on 16 consecutive rows, taking the 8-chunk rows of d = 64
+// into account); a transposed read serves 32 lanes per cycle (4 consecutive
+// rows x 4 adjacent chunks: the 4 rows must differ in bits 2-3 of swz).
+template <int D> __device__ __forceinline__ int swz(int r) {
+  return D == 64 ? 4 * ((r >> 1) & 1) + ((r >> 2) & 3) : 4 * (r & 3) + ((r >> 2) & 3);
+}
+
+// Workgroup barrier that waits for this wavefront's LDS reads only; HBM ->
+// LDS loads are waited for explicitly before the barrier that precedes their
+// first reader.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+__device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// HBM -> LDS load of a tile of R rows x D columns (16-bit) with the swizzle,
+// shared by the 256 threads of a workgroup.  Thread (wave, lane) fills chunks
+// (4 i + wave) * 64 + lane.  Rows at or past `valid` read row valid - 1 instead
+// (any finite values do: they are masked or never stored).
+template <int D, int R>
+struct TileDma {
+  static constexpr int CPR = D / 8;
+  static constexpr int LPT = R * CPR / 256;
+  static_assert(LPT >= 1 && R * CPR % 256 == 0, "tile/thread mismatch");
+  uint32_t off[LPT];  // byte offset of each chunk's source within the tile
+  int row[LPT];
+  int wave;
+  __device__ __forceinline__ void init(int gstride, int wave_, int lane) {
+    wave = wave_;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int q = (i * 4 + wave) * 64 + lane;
+      const int r = q / CPR;
+      const int p = q % CPR;
+      row[i] = r;
+      off[i] = (uint32_t)(2 * (r * gstride + (p ^ swz<D>(r)) * 8));
+    }
+  }
+  // src: first row of the tile; valid: rows of the tile that exist.
+  __device__ __forceinline__ void load(const uint16_t* src, int valid, int gstride, uint16_t* dst) const {
+    const char* s = (const char*)src;
+    if (valid >= R) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i)
+        __builtin_amdgcn_global_load_lds((gptr_t)(s + off[i]), (lptr_t)(dst + (i * 4 + wave) * 512), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const uint32_t back = (uint32_t)(2 * max(0, row[i] - (valid - 1)) * gstride);
+        __builtin_amdgcn_global_load_lds((gptr_t)(s + (off[i] - back)),
+                                         (lptr_t)(dst + (i * 4 + wave) * 512), 16, 0, 0);
+      }
+    }
+  }
+};
+
+// Per-lane LDS element offsets for reading operand fragments out of a
+// swizzled tile whose row stride is D elements.
+template <int D>
+struct FragRd {
+  // 128-bit row reads: row = 32-aligned base + l32, logical chunk 2 kk + half.
+  int row_off, row_x;
+  // transposed reads: rows 16 ks + {0, 8} + 4 half + gi / 4, elements
+  // 32 db + 16 (grp & 1) + 4 (gi & 3).
+  int tr_lo, tr_hi, x_lo, x_hi;
+  __device__ __forceinline__ void init(int lane) {
+    const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, gi = lane & 15;
+    row_off = l32 * D;
+    row_x = swz<D>(l32) ^ half;
+    const int r = 4 * half + (gi >> 2);
+    const int cl = 2 * (grp & 1) + ((gi & 3) >> 1);
+    tr_lo = r * D + 4 * (gi & 1);
+    tr_hi = (r + 8) * D + 4 * (gi & 1);
+    x_lo = swz<D>(r) ^ cl;
+    x_hi = swz<D>(r + 8) ^ cl;
+  }
+  // Hide the offsets from loop-invariant code motion (which would otherwise
+  // keep one copy of every address per LDS buffer live across the loop).
+  __device__ __forceinline__ void pin() {
+    asm volatile("" : "+v"(row_off), "+v"(row_x), "+v"(tr_lo), "+v"(tr_hi), "+v"(x_lo), "+v"(x_hi));
+  }
+  // fragment of rows [32 rb, 32 rb + 32), k-step kk (16 columns)
+  __device__ __forceinline__ frag8_t row(const uint16_t* t, int rb, int kk) const {
+    return *(const frag8_t*)(t + 32 * rb * D + row_off + (((2 * kk) ^ row_x) << 3));
+  }
+  // transposed fragment: reduction rows [16 ks, 16 ks + 16), columns [32 db, 32 db + 32)
+  __device__ __forceinline__ frag8_t tr(const uint16_t* t, int ks, int db) const {
+    const uint16_t* base = t + 16 * ks * D;
+    const s16x4_t lo = lds_read_tr(base + tr_lo + (((4 * db) ^ x_lo) << 3));
+    const s16x4_t hi = lds_read_tr(base + tr_hi + (((4 * db) ^ x_hi) << 3));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+};
+
 // ---------------------------------------------------------------------------
-// 1. D = rowsum(dO * O), dQacc = 0
+// 1. D = rowsum(dO * O)
 // ---------------------------------------------------------------------------
 template <typename Tag, int D>
 __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
@@ -54,10 +168,6 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
       acc += to_float(Tag{}, (uint16_t)(ov[i] & 0xffff)) * to_float(Tag{}, (uint16_t)(dv[i] & 0xffff));
       acc += to_float(Tag{}, (uint16_t)(ov[i] >> 16)) * to_float(Tag{}, (uint16_t)(dv[i] >> 16));
     }
-    f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-    float* q = a.dq_acc + row * D + 8 * c;
-    *(f32x4_t*)q = z;
-    *(f32x4_t*)(q + 4) = z;
   }
   // reduce over the CPR lanes of the row (CPR is a power of two <= 32)
 #pragma unroll
@@ -72,120 +182,73 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
   }
 }
 
+// Registers are budgeted for two wavefronts per SIMD up to d = 128.
+template <int D> struct BwdOcc { static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1; };
+
 // ---------------------------------------------------------------------------
-// 2. main kernel
+// 2. dK, dV: one workgroup per (batch, K/V head, 128 keys)
 // ---------------------------------------------------------------------------
-template <int D> struct BwdCfg;
-template <> struct BwdCfg<64> {
-  static constexpr int NW = 4, BM = 64;
-  static constexpr bool KV_REGS = true;
-};
-template <> struct BwdCfg<128> {
-  static constexpr int NW = 4, BM = 64;
-  static constexpr bool KV_REGS = true;
-};
-template <> struct BwdCfg<256> {
-  static constexpr int NW = 2, BM = 32;
-  static constexpr bool KV_REGS = false;
-};
+constexpr int KV_BN = 128;  // keys per workgroup (4 wavefronts x 32)
+constexpr int KV_BM = 32;   // query rows per tile
 
 template <typename Tag, int D, bool CAUSAL>
-__global__ void __launch_bounds__(BwdCfg<D>::NW * 64)
-attn_bwd_main_kernel(BwdArgs a) {
-  constexpr int NW = BwdCfg<D>::NW;
-  constexpr int NT = NW * 64;
-  constexpr int BN = NW * 32;            // keys per workgroup
-  constexpr int BM = BwdCfg<D>::BM;      // query rows per tile
-  constexpr bool KV_REGS = BwdCfg<D>::KV_REGS;
-  constexpr int QSTR = D + 16;           // Q / dO tile row stride (elements): tr reads
-  constexpr int KSTR = D + 16;           // K block row stride: tr reads (and b128 reads)
-  constexpr int SSTR = BN + 8;           // dS tile row stride: b128 reads
-  constexpr int NKK = D / 16;            // k-steps over d
-  constexpr int NQB = BM / 32;           // 32-query blocks per tile
-  constexpr int NDB = D / 32;            // 32-wide d blocks
-  constexpr int NKS = BM / 16;           // k-steps over queries (dV, dK)
-  constexpr int CPR = D / 8;
-  constexpr int TCPT = BM * CPR / NT;    // Q (and dO) tile chunks per thread
-  constexpr int KCPT = BN * CPR / NT;    // K (and V) block chunks per thread
-  constexpr int DQ_BLOCKS = NQB * NDB / NW;  // 32x32 dQ blocks per wavefront
-  static_assert(TCPT >= 1 && BM * CPR % NT == 0 && KCPT >= 1 && DQ_BLOCKS >= 1 &&
-                NQB * NDB % NW == 0, "tile/thread mismatch");
+__global__ void __launch_bounds__(256, BwdOcc<D>::WAVES_PER_SIMD)
+attn_bwd_dkdv_kernel(BwdArgs a) {
+  constexpr int TQ = KV_BM * D;   // elements of one Q (or dO) tile
+  constexpr int NKK = D / 16;     // k-steps over d
+  constexpr int NDB = D / 32;     // 32-wide d blocks
+  // V stays in LDS at d >= 128 (its B-operand fragments would not fit in
+  // registers next to the dK/dV accumulators); at d = 64 it is in registers.
+  constexpr bool V_LDS = D >= 128;
 
-  constexpr int QT = BM * QSTR;          // one Q (or dO) tile
-  constexpr int ST = BM * SSTR;          // one dS tile
-  constexpr int KB = BN * KSTR;          // the K (or V) block
-  // LDS: [Q,dO] x 2 buffers | dS x 2 buffers | K block | V block (if not in regs) | lse2, delta x 2
-  constexpr int LDS_ELEMS = 4 * QT + 2 * ST + KB + (KV_REGS ? 0 : KB);
-  __shared__ __attribute__((aligned(16))) uint16_t smem[LDS_ELEMS];
-  __shared__ __attribute__((aligned(16))) float s_lse[2][BM];
-  __shared__ __attribute__((aligned(16))) float s_del[2][BM];
+  __shared__ __attribute__((aligned(1024))) uint16_t q0s[TQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t q1s[TQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t o0s[TQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t o1s[TQ];
+  __shared__ __attribute__((aligned(1024))) uint16_t vblk[V_LDS ? KV_BN * D : 8];
+  __shared__ __attribute__((aligned(16))) float lse0[KV_BM], lse1[KV_BM], del0[KV_BM], del1[KV_BM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;
   const int l32 = lane & 31;
-  const int grp = lane >> 4;
-  const int gi = lane & 15;
 
   // ---- which (batch, kv head, key block) this workgroup owns ----
-  const int nkb = (a.N + BN - 1) / BN;
+  const int nkb = (a.N + KV_BN - 1) / KV_BN;
   const int total = nkb * a.Hkv * a.B;
   const int Lw = xcd_remap(blockIdx.x, total);
   const int bg = Lw / nkb;
   const int kb = Lw - bg * nkb;
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
-  const int k0 = kb * BN;                // first key of the block
-  const int kw0 = k0 + wave * 32;        // first key of this wavefront
-  const int mykey = kw0 + l32;           // this lane's key (C-layout column)
+  const int k0 = kb * KV_BN;           // first key of the block
+  const int kw0 = k0 + wave * 32;      // first key of this wavefront
+  const int mykey = kw0 + l32;         // this lane's key (C-layout column)
 
-  const size_t q_row = (size_t)a.Hq * D;
-  const size_t kv_row = (size_t)a.Hkv * D;
+  const int q_row = a.Hq * D;
+  const int kv_row = a.Hkv * D;
   const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.N * a.Hkv + g) * D;
   const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.N * a.Hkv + g) * D;
 
-  uint16_t* const s_k = smem + 4 * QT + 2 * ST;
-  uint16_t* const s_v = s_k + KB;  // used only when !KV_REGS
-
-  // ---- stage the K (and V) block in LDS; zeros past the sequence end ----
-#pragma unroll
-  for (int i = 0; i < KCPT; ++i) {
-    const int cidx = tid + i * NT;
-    const int r = cidx / CPR;
-    const int col = (cidx - r * CPR) * 8;
-    const int key = k0 + r;
-    u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-    if (key < a.N) {
-      kx = *(const u32x4_t*)(kbase + (size_t)key * kv_row + col);
-      if (!KV_REGS) vx = *(const u32x4_t*)(vbase + (size_t)key * kv_row + col);
-    }
-    *(u32x4_t*)(s_k + r * KSTR + col) = kx;
-    if (!KV_REGS) *(u32x4_t*)(s_v + r * KSTR + col) = vx;
-  }
-  // K / V fragments as B operands (lane = key, 8 consecutive d per k-step)
-  frag8_t kf[KV_REGS ? NKK : 1], vf[KV_REGS ? NKK : 1];
-  if (KV_REGS) {
-    const bool ok = mykey < a.N;
+  // K (and V if in registers) as B operands: lane = key, 8 consecutive d per k-step
+  frag8_t kf[NKK], vf[V_LDS ? 1 : NKK];
+  {
+    const uint16_t* kr = kbase + (size_t)min(mykey, a.N - 1) * kv_row + 8 * half;
+    const uint16_t* vr = vbase + (size_t)min(mykey, a.N - 1) * kv_row + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      u32x4_t kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-      if (ok) {
-        kx = *(const u32x4_t*)(kbase + (size_t)mykey * kv_row + 16 * kk + 8 * half);
-        vx = *(const u32x4_t*)(vbase + (size_t)mykey * kv_row + 16 * kk + 8 * half);
-      }
-      kf[KV_REGS ? kk : 0] = __builtin_bit_cast(frag8_t, kx);
-      vf[KV_REGS ? kk : 0] = __builtin_bit_cast(frag8_t, vx);
+      kf[kk] = *(const frag8_t*)(kr + 16 * kk);
+      if (!V_LDS) vf[V_LDS ? 0 : kk] = *(const frag8_t*)(vr + 16 * kk);
     }
   }
-  auto kfrag = [&](int kk) -> frag8_t {
-    if (KV_REGS) return kf[KV_REGS ? kk : 0];
-    return *(const frag8_t*)(s_k + (wave * 32 + l32) * KSTR + 16 * kk + 8 * half);
-  };
-  auto vfrag = [&](int kk) -> frag8_t {
-    if (KV_REGS) return vf[KV_REGS ? kk : 0];
-    return *(const frag8_t*)(s_v + (wave * 32 + l32) * KSTR + 16 * kk + 8 * half);
-  };
+  FragRd<D> fr;
+  fr.init(lane);
+  if (V_LDS) {  // the V block, [key][d], swizzled; read as B operand (lane = key)
+    TileDma<D, KV_BN> vdma;
+    vdma.init(kv_row, wave, lane);
+    vdma.load(vbase + (size_t)k0 * kv_row, a.N - k0, kv_row, vblk);
+  }
 
   f32x16_t dk_acc[NDB], dv_acc[NDB];  // dK^T, dV^T: lane = key, rows = d
 #pragma unroll
@@ -194,180 +257,126 @@ attn_bwd_main_kernel(BwdArgs a) {
     dv_acc[i] = (f32x16_t){};
   }
 
-  const int nqt = (a.N + BM - 1) / BM;
-  const int qt0 = CAUSAL ? (k0 / BM) : 0;   // first query tile with a row >= k0
+  // query tiles: every head of the GQA group x tiles of KV_BM rows
+  // (causal: only tiles with a row >= k0)
+  const int nqt = (a.N + KV_BM - 1) / KV_BM;
+  const int qt0 = CAUSAL ? k0 / KV_BM : 0;
   const int tiles_per_head = nqt - qt0;
   const int ntiles = tiles_per_head * a.group;
-  const float c = a.scale_log2;             // scale * log2(e), signed
+  const float c = a.scale_log2;  // scale * log2(e), signed
 
-  // global -> register staging of the next (head, query tile)
-  u32x4_t qreg[TCPT], oreg[TCPT];
-  float lreg = 0.f, dreg = 0.f;
-  auto tile_coords = [&](int t, int& h, int& q0) {
+  TileDma<D, KV_BM> qdma;
+  qdma.init(q_row, wave, lane);
+  auto coords = [&](int t, int& h, int& q0) {
     const int hh = t / tiles_per_head;
     h = g * a.group + hh;
-    q0 = (qt0 + (t - hh * tiles_per_head)) * BM;
+    q0 = (qt0 + (t - hh * tiles_per_head)) * KV_BM;
   };
-  auto load_tile = [&](int t) {
+  // Q and dO tiles by DMA; LSE (in log2 units) and D of the tile's rows are
+  // read into a register by threads 0 .. 2 KV_BM - 1 (before the DMAs, so
+  // waiting for them does not wait for the tiles) and stored to LDS at the
+  // end of the step.
+  float lsd_reg = 0.f;
+  auto load = [&](int t, uint16_t* qs, uint16_t* os) {
     int h, q0;
-    tile_coords(t, h, q0);
-    const uint16_t* qb = (const uint16_t*)a.q + ((size_t)b * a.N * a.Hq + h) * D;
-    const uint16_t* db = (const uint16_t*)a.dout + ((size_t)b * a.N * a.Hq + h) * D;
-#pragma unroll
-    for (int i = 0; i < TCPT; ++i) {
-      const int cidx = tid + i * NT;
-      const int r = cidx / CPR;
-      const int col = (cidx - r * CPR) * 8;
+    coords(t, h, q0);
+    if (tid < 2 * KV_BM) {
+      const int r = tid & (KV_BM - 1);
       const int qr = q0 + r;
-      u32x4_t qx = {0u, 0u, 0u, 0u}, dx = {0u, 0u, 0u, 0u};
-      if (qr < a.N) {
-        qx = *(const u32x4_t*)(qb + (size_t)qr * q_row + col);
-        dx = *(const u32x4_t*)(db + (size_t)qr * q_row + col);
-      }
-      qreg[i] = qx;
-      oreg[i] = dx;
-    }
-    if (tid < BM) {
-      const int qr = q0 + tid;
-      const size_t li = ((size_t)b * a.Hq + h) * a.N + qr;
+      const size_t li = ((size_t)b * a.Hq + h) * a.N + min(qr, a.N - 1);
       // rows past the end get LSE = +inf, so their probabilities are 0
-      lreg = qr < a.N ? a.lse[li] * 1.4426950408889634f : INFINITY;
-      dreg = qr < a.N ? a.delta[li] : 0.f;
+      if (tid < KV_BM) lsd_reg = qr < a.N ? a.lse[li] * 1.4426950408889634f : INFINITY;
+      else lsd_reg = a.delta[li];
     }
+    const size_t rowbase = ((size_t)b * a.N + q0) * a.Hq + h;
+    qdma.load((const uint16_t*)a.q + rowbase * D, a.N - q0, q_row, qs);
+    qdma.load((const uint16_t*)a.dout + rowbase * D, a.N - q0, q_row, os);
   };
-  auto store_tile = [&](int buf) {
-    uint16_t* sq = smem + buf * 2 * QT;
-    uint16_t* sd = sq + QT;
-#pragma unroll
-    for (int i = 0; i < TCPT; ++i) {
-      const int cidx = tid + i * NT;
-      const int r = cidx / CPR;
-      const int col = (cidx - r * CPR) * 8;
-      *(u32x4_t*)(sq + r * QSTR + col) = qreg[i];
-      *(u32x4_t*)(sd + r * QSTR + col) = oreg[i];
-    }
-    if (tid < BM) {
-      s_lse[buf][tid] = lreg;
-      s_del[buf][tid] = dreg;
-    }
+  auto store_lsd = [&](float* ls, float* ds) {
+    if (tid < KV_BM) ls[tid] = lsd_reg;
+    else if (tid < 2 * KV_BM) ds[tid - KV_BM] = lsd_reg;
   };
 
-  if (ntiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = 0; t < ntiles; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < ntiles) load_tile(t + 1);
+  // Causal: the mask is a branch-free select on every tile (cheap next to the
+  // 32 products of a tile), so one tile body serves all tiles.
+  auto tile = [&](int t, const uint16_t* qs, const uint16_t* os, const float* ls, const float* dls)
+      __attribute__((always_inline)) {
     int h, q0;
-    tile_coords(t, h, q0);
-    const uint16_t* sq = smem + buf * 2 * QT;
-    const uint16_t* sd = sq + QT;
-    uint16_t* sds = smem + 4 * QT + buf * ST;
-    const bool need_mask = CAUSAL && q0 < kw0 + 31;
-
-    // transposed-read base for A = Q^T / dO^T (lane = d, 8 query slots per k-step)
-    const int tr_off = (4 * half + (gi >> 2)) * QSTR + 16 * (grp & 1) + 4 * (gi & 3);
-
+    coords(t, h, q0);
+    (void)h;
+    // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys
+    f32x16_t s = {}, dp = {};
 #pragma unroll
-    for (int qb = 0; qb < NQB; ++qb) {
-      // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys
-      f32x16_t s = {}, dp = {};
-      const uint16_t* qrow = sq + (32 * qb + l32) * QSTR + 8 * half;
-      const uint16_t* drow = sd + (32 * qb + l32) * QSTR + 8 * half;
+    for (int kk = 0; kk < NKK; ++kk) {
+      s = mfma32(Tag{}, fr.row(qs, 0, kk), kf[kk], s);
+      const frag8_t vv = V_LDS ? fr.row(vblk, wave, kk) : vf[V_LDS ? 0 : kk];
+      dp = mfma32(Tag{}, fr.row(os, 0, kk), vv, dp);
+    }
+    // P = 2^(S c - LSE2), dS = P (dP - D); C rows = queries 8 (r / 4) + 4 half + r % 4
+    const int klim = mykey - q0 - 4 * half;
+    uint32_t pw[8], dsw[8];
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s = mfma32(Tag{}, *(const frag8_t*)(qrow + 16 * kk), kfrag(kk), s);
-        dp = mfma32(Tag{}, *(const frag8_t*)(drow + 16 * kk), vfrag(kk), dp);
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const f32x4_t l4 = *(const f32x4_t*)(ls + 8 * r4 + 4 * half);
+      const f32x4_t d4 = *(const f32x4_t*)(dls + 8 * r4 + 4 * half);
+      float p[4], dsv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * r4 + e;
+        float pv = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
+        if (CAUSAL) pv = (8 * r4 + e) < klim ? 0.f : pv;  // query < key
+        p[e] = pv;
+        dsv[e] = pv * (dp[r] - d4[e]);
       }
-      // P = 2^(S c - LSE log2 e), dS = P (dP - D); rows = queries 8(r/4) + 4h + r%4
-      const float* lsep = &s_lse[buf][32 * qb + 4 * half];
-      const float* delp = &s_del[buf][32 * qb + 4 * half];
-      uint32_t pw[8], dsw[8];
+      pw[2 * r4] = pack2(Tag{}, p[0], p[1]);
+      pw[2 * r4 + 1] = pack2(Tag{}, p[2], p[3]);
+      dsw[2 * r4] = pack2(Tag{}, dsv[0], dsv[1]);
+      dsw[2 * r4 + 1] = pack2(Tag{}, dsv[2], dsv[3]);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries (two k-steps)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4_t l4 = *(const f32x4_t*)(lsep + 8 * r4);
-        const f32x4_t d4 = *(const f32x4_t*)(delp + 8 * r4);
-        float p[4], ds[4];
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4_t p4 = {pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]};
+      const u32x4_t d4 = {dsw[4 * ks], dsw[4 * ks + 1], dsw[4 * ks + 2], dsw[4 * ks + 3]};
+      const frag8_t pfrag = __builtin_bit_cast(frag8_t, p4);
+      const frag8_t dsfrag = __builtin_bit_cast(frag8_t, d4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          float pv = fast_exp2(s[r] * c - l4[e]);
-          if (need_mask) {
-            const int qi = q0 + 32 * qb + 8 * r4 + 4 * half + e;
-            if (mykey > qi) pv = 0.f;
-          }
-          p[e] = pv;
-          ds[e] = pv * (dp[r] - d4[e]);
-        }
-        pw[2 * r4] = pack2(Tag{}, p[0], p[1]);
-        pw[2 * r4 + 1] = pack2(Tag{}, p[2], p[3]);
-        dsw[2 * r4] = pack2(Tag{}, ds[0], ds[1]);
-        dsw[2 * r4 + 1] = pack2(Tag{}, ds[2], ds[3]);
-      }
-      // dS -> LDS as [query][key] for dQ = dS K (rows 8(r/4) + 4h + e, column = key)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int qi = 32 * qb + 8 * r4 + 4 * half + e;
-          const uint32_t w = dsw[2 * r4 + (e >> 1)];
-          sds[qi * SSTR + wave * 32 + l32] = (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffff));
-        }
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS  (k-steps over this block's 32 queries)
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const u32x4_t pv4 = {pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]};
-        const u32x4_t dv4 = {dsw[4 * ks], dsw[4 * ks + 1], dsw[4 * ks + 2], dsw[4 * ks + 3]};
-        const frag8_t pfrag = __builtin_bit_cast(frag8_t, pv4);
-        const frag8_t dsfrag = __builtin_bit_cast(frag8_t, dv4);
-        const int rowoff = (32 * qb + 16 * ks) * QSTR + tr_off;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const uint16_t* pd = sd + rowoff + 32 * db;
-          const uint16_t* pq = sq + rowoff + 32 * db;
-          const frag8_t dof = __builtin_shufflevector(lds_read_tr(pd), lds_read_tr(pd + 8 * QSTR),
-                                                      0, 1, 2, 3, 4, 5, 6, 7);
-          const frag8_t qtf = __builtin_shufflevector(lds_read_tr(pq), lds_read_tr(pq + 8 * QSTR),
-                                                      0, 1, 2, 3, 4, 5, 6, 7);
-          dv_acc[db] = mfma32(Tag{}, dof, pfrag, dv_acc[db]);
-          dk_acc[db] = mfma32(Tag{}, qtf, dsfrag, dk_acc[db]);
-        }
+      for (int db = 0; db < NDB; ++db) {
+        dv_acc[db] = mfma32(Tag{}, fr.tr(os, ks, db), pfrag, dv_acc[db]);
+        dk_acc[db] = mfma32(Tag{}, fr.tr(qs, ks, db), dsfrag, dk_acc[db]);
       }
     }
-    if (t + 1 < ntiles) store_tile(buf ^ 1);
-    __syncthreads();  // dS tile complete (and the next Q/dO tile staged)
+  };
 
-    // dQacc[q0 .. q0+BM) += dS K over this block's BN keys
-    float* dqb = a.dq_acc + ((size_t)b * a.N * a.Hq + h) * D;
-#pragma unroll
-    for (int blk = 0; blk < DQ_BLOCKS; ++blk) {
-      const int id = wave * DQ_BLOCKS + blk;
-      const int qb = id / NDB;
-      const int db = id - qb * NDB;
-      f32x16_t acc = {};
-      const uint16_t* arow = sds + (32 * qb + l32) * SSTR + 8 * half;
-      // B = K[key][d]: lane = d, keys 16s + 8h + 4a + j via transposed reads
-      const uint16_t* kb_rd = s_k + (8 * half + (gi >> 2)) * KSTR + 32 * db + 16 * (grp & 1) + 4 * (gi & 3);
-#pragma unroll
-      for (int ks = 0; ks < BN / 16; ++ks) {
-        const frag8_t af = *(const frag8_t*)(arow + 16 * ks);
-        const uint16_t* p = kb_rd + 16 * ks * KSTR;
-        const frag8_t bf = __builtin_shufflevector(lds_read_tr(p), lds_read_tr(p + 4 * KSTR),
-                                                   0, 1, 2, 3, 4, 5, 6, 7);
-        acc = mfma32(Tag{}, af, bf, acc);
-      }
-      // C: lane = d column (32 db + l32), rows = queries 32 qb + 8(r/4) + 4h + r%4
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = q0 + 32 * qb + 8 * (r >> 2) + 4 * half + (r & 3);
-        if (qi < a.N) atomicAdd(dqb + (size_t)qi * q_row + 32 * db + l32, acc[r]);
-      }
-    }
+  // Tile t lives in buffer t & 1; one barrier per tile, the same number for
+  // every wavefront.
+  if (ntiles > 0) {
+    load(0, q0s, o0s);
+    store_lsd(lse0, del0);
   }
+  wait_loads();
+  __syncthreads();
+  auto step = [&](int t, int buf) __attribute__((always_inline)) {
+    if (t + 1 < ntiles) {
+      if (buf) load(t + 1, q0s, o0s);
+      else load(t + 1, q1s, o1s);
+    }
+    fr.pin();
+    if (buf) tile(t, q1s, o1s, lse1, del1);
+    else tile(t, q0s, o0s, lse0, del0);
+    if (t + 1 < ntiles) {
+      if (buf) store_lsd(lse0, del0);
+      else store_lsd(lse1, del1);
+    }
+    wait_loads();
+    __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < ntiles; t += 2) {
+    step(t, 0);
+    step(t + 1, 1);
+  }
+  if (t < ntiles) step(t, 0);
 
   // ---- epilogue: dK = scale * dK_acc, dV = dV_acc; lane = key, rows = d ----
   if (mykey < a.N) {
@@ -389,18 +398,180 @@ attn_bwd_main_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// 3. dQ = scale * dQacc -> input dtype
+// 3. dQ: one workgroup per (batch, query head, 128 queries)
 // ---------------------------------------------------------------------------
-template <typename Tag>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(BwdArgs a, long long nchunks) {
-  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;  // 8-element chunk index
-  if (i >= nchunks) return;
-  const f32x4_t x0 = *(const f32x4_t*)(a.dq_acc + 8 * i);
-  const f32x4_t x1 = *(const f32x4_t*)(a.dq_acc + 8 * i + 4);
-  const float s = a.scale;
-  const u32x4_t w = {pack2(Tag{}, x0[0] * s, x0[1] * s), pack2(Tag{}, x0[2] * s, x0[3] * s),
-                     pack2(Tag{}, x1[0] * s, x1[1] * s), pack2(Tag{}, x1[2] * s, x1[3] * s)};
-  *(u32x4_t*)((uint16_t*)a.dq + 8 * i) = w;
+constexpr int DQ_BM = 128;  // queries per workgroup (4 wavefronts x 32)
+
+template <typename Tag, int D, bool CAUSAL>
+__global__ void __launch_bounds__(256, BwdOcc<D>::WAVES_PER_SIMD)
+attn_bwd_dq_kernel(BwdArgs a) {
+  constexpr int BN = 8192 / D;   // keys per tile (each K / V tile is 16 KiB)
+  constexpr int TILE = BN * D;
+  constexpr int NKK = D / 16;
+  constexpr int NSB = BN / 32;   // 32-key sub-blocks per tile
+  constexpr int NDB = D / 32;
+  constexpr int NKS = BN / 16;   // k-steps over keys in dQ^T += K^T dS^T
+
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int l32 = lane & 31;
+
+  // ---- which (batch, head, row block) this workgroup owns; heaviest first ----
+  const int nblk = (a.N + DQ_BM - 1) / DQ_BM;
+  const int total = nblk * a.Hq * a.B;
+  const int L = xcd_remap(blockIdx.x, total);
+  const int bh = L / nblk;
+  const int rb = nblk - 1 - (L - bh * nblk);
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int g = h / a.group;
+
+  const int q_row = a.Hq * D;
+  const int kv_row = a.Hkv * D;
+  const int row0 = rb * DQ_BM;
+  const int wrow0 = row0 + wave * 32;
+  const int qrow = wrow0 + l32;
+  const int qsafe = min(qrow, a.N - 1);
+
+  // Q and dO as B operands (lane = query, 8 consecutive d per k-step)
+  frag8_t qf[NKK], of[NKK];
+  {
+    const size_t ro = ((size_t)b * a.N + qsafe) * a.Hq + h;
+    const uint16_t* qr = (const uint16_t*)a.q + ro * D + 8 * half;
+    const uint16_t* orr = (const uint16_t*)a.dout + ro * D + 8 * half;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qf[kk] = *(const frag8_t*)(qr + 16 * kk);
+      of[kk] = *(const frag8_t*)(orr + 16 * kk);
+    }
+  }
+  const size_t li = ((size_t)b * a.Hq + h) * a.N + qsafe;
+  const float lse2 = a.lse[li] * 1.4426950408889634f;
+  const float dlt = a.delta[li];
+  const float c = a.scale_log2;  // scale * log2(e), signed
+
+  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.N * a.Hkv + g) * D;
+  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.N * a.Hkv + g) * D;
+  TileDma<D, BN> dma;
+  dma.init(kv_row, wave, lane);
+  FragRd<D> fr;
+  fr.init(lane);
+
+  const int ntiles_all = (a.N + BN - 1) / BN;
+  int ntiles = ntiles_all, nwave = ntiles_all, nfull = a.N / BN;
+  if (CAUSAL) {
+    ntiles = min(ntiles_all, (min(row0 + DQ_BM, a.N) - 1) / BN + 1);
+    nwave = min(ntiles_all, (wrow0 + 31) / BN + 1);
+    nfull = min(nfull, (wrow0 + 1) / BN);
+  }
+
+  f32x16_t dq_acc[NDB];  // dQ^T: lane = query, rows = d
+#pragma unroll
+  for (int i = 0; i < NDB; ++i) dq_acc[i] = (f32x16_t){};
+
+  auto load = [&](int j, uint16_t* ks, uint16_t* vs) {
+    const size_t off = (size_t)j * BN * kv_row;
+    dma.load(kbase + off, a.N - j * BN, kv_row, ks);
+    dma.load(vbase + off, a.N - j * BN, kv_row, vs);
+  };
+
+  auto tile = [&](int j, const uint16_t* ks, const uint16_t* vs, auto mask_tag)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    // Per 32-key sub-block: S^T = K Q^T and dP^T = V dO^T for this
+    // wavefront's 32 queries, then dS^T = P^T (dP^T - D) with
+    // P^T = 2^(S^T c - LSE2); rows = keys 32 sb + 8 (r / 4) + 4 half + r % 4.
+    const int key0 = j * BN;
+    int lim = 0;
+    if (MASK) {
+      lim = a.N - 1 - key0 - 4 * half;
+      if (CAUSAL) lim = min(lim, qrow - key0 - 4 * half);
+    }
+    frag8_t dsf[NKS];
+#pragma unroll
+    for (int sb = 0; sb < NSB; ++sb) {
+      f32x16_t s = {}, dp = {};
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s = mfma32(Tag{}, fr.row(ks, sb, kk), qf[kk], s);
+        dp = mfma32(Tag{}, fr.row(vs, sb, kk), of[kk], dp);
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t w[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const int r = 8 * hh + 2 * t;
+          float p0 = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+          float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -lse2));
+          if (MASK) {
+            p0 = (32 * sb + 8 * (r >> 2) + (r & 3)) <= lim ? p0 : 0.f;
+            p1 = (32 * sb + 8 * ((r + 1) >> 2) + ((r + 1) & 3)) <= lim ? p1 : 0.f;
+          }
+          w[t] = pack2(Tag{}, p0 * (dp[r] - dlt), p1 * (dp[r + 1] - dlt));
+        }
+        const u32x4_t wv = {w[0], w[1], w[2], w[3]};
+        dsf[2 * sb + hh] = __builtin_bit_cast(frag8_t, wv);
+      }
+    }
+    // dQ^T += K^T dS^T : A operand K^T via transposed reads of the K tile
+#pragma unroll
+    for (int ksb = 0; ksb < NKS; ++ksb)
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        dq_acc[db] = mfma32(Tag{}, fr.tr(ks, ksb, db), dsf[ksb], dq_acc[db]);
+  };
+
+  load(0, k0s, v0s);
+  wait_loads();
+  barrier_lds();
+  auto step = [&](int j, int buf, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    fr.pin();
+    if (j + 1 < ntiles) {
+      if (buf) load(j + 1, k0s, v0s);
+      else load(j + 1, k1s, v1s);
+    }
+    if (!MASK || j < nwave) {
+      if (buf) tile(j, k1s, v1s, mask_tag);
+      else tile(j, k0s, v0s, mask_tag);
+    }
+    wait_loads();
+    barrier_lds();
+  };
+  // one barrier per tile for every wavefront; steady state in pairs so both
+  // buffers are compile-time objects
+  int j = 0;
+  for (; j + 1 < nfull; j += 2) {
+    step(j, 0, std::false_type{});
+    step(j + 1, 1, std::false_type{});
+  }
+  if (j < nfull) {
+    step(j, 0, std::false_type{});
+    ++j;
+  }
+  for (; j < ntiles; ++j) step(j, j & 1, std::true_type{});
+
+  // ---- epilogue: dQ = scale * dQ^T acc; lane = query, rows = d ----
+  if (qrow < a.N) {
+    uint16_t* dqr = (uint16_t*)a.dq + (((size_t)b * a.N + qrow) * a.Hq + h) * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = 32 * db + 8 * q4 + 4 * half;
+        const u32x2_t w = {pack2(Tag{}, dq_acc[db][4 * q4] * a.scale, dq_acc[db][4 * q4 + 1] * a.scale),
+                           pack2(Tag{}, dq_acc[db][4 * q4 + 2] * a.scale, dq_acc[db][4 * q4 + 3] * a.scale)};
+        *(u32x2_t*)(dqr + d0) = w;
+      }
+  }
 }
 
 }  // namespace
@@ -417,20 +588,18 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     if (e != hipSuccess) return e;
   }
   if (stages & 2) {
-    constexpr int BN = BwdCfg<D>::NW * 32;
-    const long long grid = (long long)((a.N + BN - 1) / BN) * a.Hkv * a.B;
+    const long long grid = (long long)((a.N + KV_BN - 1) / KV_BN) * a.Hkv * a.B;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_bwd_main_kernel<Tag, D, CAUSAL>), dim3((unsigned)grid),
-                       dim3(BwdCfg<D>::NW * 64), 0, stream, a);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & 4) {
-    const long long nchunks = rows * D / 8;
-    const long long grid = (nchunks + 255) / 256;
+    const long long grid = (long long)((a.N + DQ_BM - 1) / DQ_BM) * a.Hq * a.B;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag>), dim3((unsigned)grid), dim3(256), 0, stream, a,
-                       nchunks);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL>), dim3((unsigned)grid), dim3(256), 0,
+                       stream, a);
     return hipGetLastError();
   }
   return hipSuccess;

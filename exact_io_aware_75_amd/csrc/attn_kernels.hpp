@@ -29,7 +29,6 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* dq_acc;     // workspace: [B, N, Hq, d] fp32
   float* delta;      // workspace: [B, Hq, N] fp32, rowsum(dO * O)
   int B, N, Hq, Hkv;
   int group;
@@ -39,14 +38,13 @@ struct BwdArgs {
 
 // Workspace layout of the backward pass (offsets in bytes, 256-byte aligned).
 struct BwdWorkspace {
-  size_t dq_acc_off, dq_acc_bytes;
   size_t delta_off, delta_bytes;
   size_t total;
 };
 BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int Hkv, int d);
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream);
-// stage_mask: bit 0 = preprocess, bit 1 = main kernel, bit 2 = dQ conversion
+// stage_mask: bit 0 = D preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, int d, bool causal, int stage_mask,
                       hipStream_t stream);
 

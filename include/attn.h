@@ -87,8 +87,8 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              void* stream);
 
 /*
- * Bytes of device workspace attn_bwd needs for these sizes: an fp32 dQ
- * accumulator and the per-row D = rowsum(dO * O), both O(B * N * Hq * d), plus
+ * Bytes of device workspace attn_bwd needs for these sizes: the per-row
+ * D = rowsum(dO * O) in float32, B * Hq * N values (O(B * N * Hq)), plus
  * alignment.  Returns 0 if the sizes are invalid.
  */
 size_t attn_bwd_workspace_bytes(int B, int N, int Hq, int Hkv, int d);
@@ -97,12 +97,14 @@ size_t attn_bwd_workspace_bytes(int B, int N, int Hq, int Hkv, int d);
  * Backward pass.  Given the forward inputs, its outputs o and lse (from an
  * attn_fwd call with the same causal flag and scale) and the upstream gradient
  * dout, writes dq, dk, dv of L = sum(o * dout).  Scores and probabilities are
- * recomputed tile by tile from lse; the work is parallel over key/value
- * column blocks.  dk/dv of a K/V head sum the contributions of every query
- * head in its group.  `workspace` (device memory, 16-byte aligned, at least
- * attn_bwd_workspace_bytes() bytes) is scratch: its contents on entry are
- * ignored and on exit undefined.  Results are deterministic up to the order of
- * fp32 atomic additions in the dQ accumulator.
+ * recomputed tile by tile from lse (FlashAttention-1 news page, section
+ * "FlashAttention"; FlashAttention-2 announcement, section "具体实现"): dk and
+ * dv in a pass parallel over key/value column blocks, dq in a pass parallel
+ * over query row blocks.  dk/dv of a K/V head sum the contributions of every
+ * query head in its group.  `workspace` (device memory, 16-byte aligned, at
+ * least attn_bwd_workspace_bytes() bytes) is scratch: its contents on entry
+ * are ignored and on exit undefined.  No atomics are used: results are
+ * bitwise deterministic.
  */
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
              const float* lse, void* dq, void* dk, void* dv, void* workspace,
@@ -112,26 +114,26 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
 /*
  * The three stages attn_bwd runs, exposed so a caller can schedule or time
  * them separately.  Same arguments and validation as attn_bwd; they must be
- * enqueued in this order on one stream with the same workspace, and together
- * they are exactly attn_bwd:
+ * enqueued in this order on one stream with the same workspace (the last two
+ * may also be swapped), and together they are exactly attn_bwd:
  *   attn_bwd_preprocess   D = rowsum(dout * o) per query row into the
- *                         workspace, and the fp32 dQ accumulator set to zero;
- *   attn_bwd_main         the recomputation loop: dk and dv written, dQ
- *                         partial sums added into the accumulator;
- *   attn_bwd_convert_dq   dq = scale * accumulator, rounded into `dtype`.
+ *                         workspace;
+ *   attn_bwd_dkdv         recomputation over key/value column blocks: dk and
+ *                         dv written;
+ *   attn_bwd_dq           recomputation over query row blocks: dq written.
  */
 int attn_bwd_preprocess(const void* q, const void* k, const void* v, const void* o,
                         const void* dout, const float* lse, void* dq, void* dk, void* dv,
                         void* workspace, size_t workspace_bytes, int B, int N, int Hq, int Hkv,
                         int d, int dtype, int causal, float scale, void* stream);
-int attn_bwd_main(const void* q, const void* k, const void* v, const void* o, const void* dout,
+int attn_bwd_dkdv(const void* q, const void* k, const void* v, const void* o, const void* dout,
                   const float* lse, void* dq, void* dk, void* dv, void* workspace,
                   size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
                   int causal, float scale, void* stream);
-int attn_bwd_convert_dq(const void* q, const void* k, const void* v, const void* o,
-                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
-                        void* workspace, size_t workspace_bytes, int B, int N, int Hq, int Hkv,
-                        int d, int dtype, int causal, float scale, void* stream);
+int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
+                int causal, float scale, void* stream);
 
 /* Static, human-readable description of a status code. */
 const char* attn_strerror(int status);

@@ -58,6 +58,18 @@ def test_small_shapes(gpu_device, b, n, hq, hkv, d, dtype, causal):
     _check_all(x, out, causal, scale, f"b{b} n{n} hq{hq} hkv{hkv} d{d} {dtype} causal={causal}", dtype)
 
 
+def test_deterministic(gpu_device):
+    """No atomics anywhere: two runs give bitwise identical gradients."""
+    import torch
+
+    x = gen.make_inputs(2, 1000, 4, 2, 128, "bf16", cfg_id=19)
+    a = run_fwd_bwd(x, "bf16", True, 1.0 / np.sqrt(128), gpu_device)
+    b = run_fwd_bwd(x, "bf16", True, 1.0 / np.sqrt(128), gpu_device)
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+    del torch
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.1])
 def test_unusual_scales(gpu_device, scale):
     x = gen.make_inputs(1, 150, 2, 1, 64, "bf16", cfg_id=18)
