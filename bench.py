@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # MI355X dense bf16 MFMA: 256 CU x 4096 FLOP/clk x 2.4 GHz
 WORKLOAD = dict(name="hidden2048_d128", b=4, n=4096, h=16, d=128)
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_main_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_dkdv_traffic_B4_N4096_H16_d128.json")
 KERNEL_SOURCES = ("exact_io_aware_75_amd/csrc/attn_bwd.hip", "exact_io_aware_75_amd/csrc/attn_common.hpp")
 
 
@@ -290,12 +290,19 @@ def _read_csv(path):
         return list(csv.DictReader(f))
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, cmd):
-    """Turn rocprofv3 CSV output into profiles/ summaries.
+PROFILE_TAG = "B4_N4096_H16_d128"  # the benchmark workload, for profile file names
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
+    """Turn rocprofv3 CSV output of `bench.py` runs into profiles/ summaries.
 
     trace_dir: a --kernel-trace --stats run (kernel_stats.csv); fetch_dir /
-    write_dir: --pmc FETCH_SIZE and --pmc WRITE_SIZE runs (counter_collection.csv).
-    Writes profiles/bwd_main_kernel_stats.txt and profiles/bwd_main_traffic.json.
+    write_dir: --pmc FETCH_SIZE and --pmc WRITE_SIZE runs; evidence_dir: a
+    --pmc run of SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+    SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE (or None).
+    Writes profiles/step_kernels_<workload>.txt (per-kernel time, HBM bytes,
+    MFMA busy, LDS conflicts) and profiles/bwd_dkdv_traffic_<workload>.json
+    (the dominant kernel's HBM bytes per launch, read back by the benchmark).
     """
     import glob
 
@@ -305,55 +312,79 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, cmd):
             raise SystemExit(f"no {pattern} under {d}")
         return hits[0]
 
-    stats = _read_csv(find(trace_dir, "*kernel_stats.csv"))
-    lines = [f"rocprofv3 --kernel-trace --stats summary (command: {cmd['trace']})", ""]
-    lines.append(f"{'kernel':100s} {'calls':>6s} {'avg_us':>10s} {'pct':>6s}")
-    for r in stats:
-        lines.append(f"{r['Name'][:100]:100s} {r['Calls']:>6s} {float(r['AverageNs']) / 1e3:10.2f} "
-                     f"{float(r['Percentage']):6.2f}")
-
-    def per_kernel(d, counter):
+    def per_kernel(d, counters):
         rows = _read_csv(find(d, "*counter_collection.csv"))
         acc = {}
         for r in rows:
-            if r.get("Counter_Name") != counter:
+            if r.get("Counter_Name") not in counters:
                 continue
-            acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
-        return {k_: sum(v_) / len(v_) for k_, v_ in acc.items()}
+            acc.setdefault(r["Kernel_Name"], {}).setdefault(r["Counter_Name"], []).append(
+                float(r["Counter_Value"]))
+        return {k_: {c_: sum(v_) / len(v_) for c_, v_ in cs.items()} for k_, cs in acc.items()}
 
-    fetch = per_kernel(fetch_dir, "FETCH_SIZE")
-    write = per_kernel(write_dir, "WRITE_SIZE")
-
-    def pick(table, key):
-        for name, val in table.items():
-            if key(name):
-                return name, val
-        raise SystemExit(f"kernel not found in counters: {list(table)[:5]}")
+    stats = _read_csv(find(trace_dir, "*kernel_stats.csv"))
+    fetch = per_kernel(fetch_dir, {"FETCH_SIZE"})
+    write = per_kernel(write_dir, {"WRITE_SIZE"})
+    evid = per_kernel(evidence_dir, {"SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
+                                     "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
+                                     "GRBM_GUI_ACTIVE"}) if evidence_dir else {}
 
     is_copy = lambda nm: "elementwise" in nm.lower() and "neg" in nm.lower()  # noqa: E731
-    is_main = lambda nm: "attn_bwd_main_kernel" in nm and (  # noqa: E731
-        "Bf16Tag, 128, false" in nm or "Bf16TagELi128ELb0E" in nm)
-    cname, cf = pick(fetch, is_copy)
-    _, cw = pick(write, is_copy)
-    mname, mf = pick(fetch, is_main)
-    _, mw = pick(write, is_main)
+    cname = next(k_ for k_ in fetch if is_copy(k_))
+    cf, cw = fetch[cname]["FETCH_SIZE"], write[cname]["WRITE_SIZE"]
     f_scale = COPY_BYTES / (cf * 1024.0)
     w_scale = COPY_BYTES / (cw * 1024.0)
-    read_b = mf * 1024.0 * f_scale
-    write_b = mw * 1024.0 * w_scale
-    lines += ["", f"HBM traffic (commands: {cmd['fetch']} ; {cmd['write']})",
-              f"calibration kernel {cname[:80]}: FETCH_SIZE {cf:.0f} KiB, WRITE_SIZE {cw:.0f} KiB for "
-              f"{COPY_BYTES} B each -> scale {f_scale:.4f} / {w_scale:.4f}",
-              f"{mname[:100]}: FETCH_SIZE {mf:.0f} KiB, WRITE_SIZE {mw:.0f} KiB per dispatch -> "
-              f"{read_b / 1e6:.1f} MB read + {write_b / 1e6:.1f} MB written per launch"]
+
+    def short(nm):
+        nm = nm.replace("(anonymous namespace)::", "").replace("attn::", "")
+        return nm[nm.find("attn_"):nm.find("(")] if "attn_" in nm else nm[:60]
+
+    lines = [f"Kernels of one benchmark step (workload {PROFILE_TAG}, bf16; fwd + bwd, non-causal and causal)",
+             "",
+             f"trace:    {cmd.get('trace', '')}",
+             f"fetch:    {cmd.get('fetch', '')}",
+             f"write:    {cmd.get('write', '')}",
+             f"evidence: {cmd.get('evidence', '')}",
+             "",
+             f"HBM counter calibration: plain copy of {COPY_BYTES} B reads FETCH_SIZE {cf:.0f} KiB, "
+             f"WRITE_SIZE {cw:.0f} KiB -> byte scale {f_scale:.4f} (fetch) / {w_scale:.4f} (write)",
+             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+             "MFMA FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512",
+             "",
+             f"{'kernel':52s} {'calls':>5s} {'avg_us':>9s} {'pct':>6s} {'HBM_rd_MB':>10s} {'HBM_wr_MB':>10s} "
+             f"{'HBM_GB/s':>9s} {'MFMA_busy':>9s} {'MFMA_TFLOP':>10s} {'LDS_confl':>9s}"]
+    dom = None
+    for r in stats:
+        nm = r["Name"]
+        if "attn_" not in nm:
+            continue
+        avg_us = float(r["AverageNs"]) / 1e3
+        fk = next((v_ for k_, v_ in fetch.items() if k_ == nm), {})
+        wk = next((v_ for k_, v_ in write.items() if k_ == nm), {})
+        ek = next((v_ for k_, v_ in evid.items() if k_ == nm), {})
+        rd = fk.get("FETCH_SIZE", float("nan")) * 1024.0 * f_scale
+        wr = wk.get("WRITE_SIZE", float("nan")) * 1024.0 * w_scale
+        gbs = (rd + wr) / (avg_us * 1e-6) / 1e9
+        busy = conf = tf = float("nan")
+        if ek:
+            busy = ek["SQ_VALU_MFMA_BUSY_CYCLES"] * 8 / (ek["GRBM_GUI_ACTIVE"] * 1024.0)
+            tf = ek["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e12
+            conf = ek["SQ_LDS_BANK_CONFLICT"] / max(1.0, ek["SQ_LDS_IDX_ACTIVE"])
+        lines.append(f"{short(nm)[:52]:52s} {r['Calls']:>5s} {avg_us:9.2f} {float(r['Percentage']):6.2f} "
+                     f"{rd / 1e6:10.1f} {wr / 1e6:10.1f} {gbs:9.1f} {busy:9.3f} {tf:10.4f} {conf:9.4f}")
+        if "attn_bwd_dkdv_kernel" in nm and ("128, false" in nm or "Li128ELb0E" in nm):
+            dom = (nm, rd, wr, fk.get("FETCH_SIZE"), wk.get("WRITE_SIZE"), avg_us)
+    if dom is None:
+        raise SystemExit("dK/dV kernel (d=128, non-causal) not found in the trace")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    with open(os.path.join(ROOT, "profiles", "bwd_main_kernel_stats.txt"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", f"step_kernels_{PROFILE_TAG}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
+    nm, rd, wr, fkib, wkib, avg_us = dom
     with open(TRAFFIC_FILE, "w") as f:
-        json.dump({"kernel": mname, "source_sha256": kernel_source_hash(),
-                   "fetch_kib": mf, "write_kib": mw, "copy_fetch_kib": cf, "copy_write_kib": cw,
-                   "copy_bytes": COPY_BYTES, "read_bytes": read_b, "write_bytes": write_b,
-                   "bytes_per_launch": read_b + write_b, "commands": cmd}, f, indent=1)
+        json.dump({"kernel": nm, "source_sha256": kernel_source_hash(), "avg_us_rocprof": avg_us,
+                   "fetch_kib": fkib, "write_kib": wkib, "copy_fetch_kib": cf, "copy_write_kib": cw,
+                   "copy_bytes": COPY_BYTES, "read_bytes": rd, "write_bytes": wr,
+                   "bytes_per_launch": rd + wr, "commands": cmd}, f, indent=1)
     print("\n".join(lines))
 
 
@@ -368,7 +399,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain copy of known size first (for counter calibration)")
-    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+    ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "EVIDENCE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output and exit")
     ap.add_argument("--summarize-cmds", default="{}", help="JSON dict of the commands that made them")
     args = ap.parse_args()
