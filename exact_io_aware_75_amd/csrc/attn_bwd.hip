@@ -272,29 +272,30 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     h = g * a.group + hh;
     q0 = (qt0 + (t - hh * tiles_per_head)) * KV_BM;
   };
-  // Q and dO tiles by DMA; LSE (in log2 units) and D of the tile's rows are
-  // read into a register by threads 0 .. 2 KV_BM - 1 (before the DMAs, so
-  // waiting for them does not wait for the tiles) and stored to LDS at the
-  // end of the step.
-  float lsd_reg = 0.f;
+  // Q and dO tiles by DMA.  LSE and D of the tile's rows are loaded raw into
+  // a register by threads 0 .. 2 KV_BM - 1 (LSE by the first KV_BM, D by the
+  // rest) and only converted and stored to LDS at the end of the step, so
+  // nothing waits for the load before the tile's products.
+  float lsd_raw = 0.f;
+  bool lsd_valid = false;
   auto load = [&](int t, uint16_t* qs, uint16_t* os) {
     int h, q0;
     coords(t, h, q0);
     if (tid < 2 * KV_BM) {
-      const int r = tid & (KV_BM - 1);
-      const int qr = q0 + r;
+      const int qr = q0 + (tid & (KV_BM - 1));
       const size_t li = ((size_t)b * a.Hq + h) * a.N + min(qr, a.N - 1);
-      // rows past the end get LSE = +inf, so their probabilities are 0
-      if (tid < KV_BM) lsd_reg = qr < a.N ? a.lse[li] * 1.4426950408889634f : INFINITY;
-      else lsd_reg = a.delta[li];
+      const float* src = tid < KV_BM ? a.lse : a.delta;
+      lsd_raw = src[li];
+      lsd_valid = qr < a.N;
     }
     const size_t rowbase = ((size_t)b * a.N + q0) * a.Hq + h;
     qdma.load((const uint16_t*)a.q + rowbase * D, a.N - q0, q_row, qs);
     qdma.load((const uint16_t*)a.dout + rowbase * D, a.N - q0, q_row, os);
   };
   auto store_lsd = [&](float* ls, float* ds) {
-    if (tid < KV_BM) ls[tid] = lsd_reg;
-    else if (tid < 2 * KV_BM) ds[tid - KV_BM] = lsd_reg;
+    // LSE in log2 units; rows past the end get +inf, so their probabilities are 0
+    if (tid < KV_BM) ls[tid] = lsd_valid ? lsd_raw * 1.4426950408889634f : INFINITY;
+    else if (tid < 2 * KV_BM) ds[tid - KV_BM] = lsd_raw;
   };
 
   // Causal: the mask is a branch-free select on every tile (cheap next to the
