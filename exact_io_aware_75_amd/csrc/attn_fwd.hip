@@ -25,19 +25,28 @@
 //
 // CDNA4 mapping.
 //  * Occupancy: two workgroups of four wavefronts per CU (two wavefronts per
-//    SIMD, <= 256 registers each), so one wavefront's softmax (VALU) runs
-//    while the other's matrix products (MFMA) run on the same SIMD.
+//    SIMD, <= 256 registers each).
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 //    accumulator holds one query per lane and 16 keys per register block, so
 //    the row max / row sum are in-lane except one v_permlane32_swap between
 //    lanes l and l ^ 32, and the probabilities are already the B operand of
 //    O^T += V^T P^T.  V^T comes from the row-major V tile through
 //    ds_read_b64_tr_b16.  Q stays in registers for the whole loop.
-//  * K/V tiles go HBM -> LDS by global_load_lds_dwordx4 (no register staging),
-//    double-buffered: the next tile's loads are in flight while the current
-//    one is consumed.  The LDS tiles are unpadded and XOR-swizzled in 16-byte
-//    chunks so that both the 128-bit K reads and the transposed V reads are
-//    free of bank conflicts.
+//  * Software pipeline inside each wavefront: while the matrix cores form
+//    the scores of key tile j + 1, the VALU reduces the row max of tile j and
+//    exponentiates the first half of its probabilities; the second half is
+//    exponentiated under the first half of tile j's P V products.  A single
+//    wavefront's VALU work thus issues in the shadow of its own MFMAs instead
+//    of waiting for the other wavefront on the SIMD.  The key tiles after the
+//    last unmasked one (the diagonal and the ragged end) run unpipelined.
+//  * K/V tiles go HBM -> LDS by buffer_load_dwordx4 ... lds (no register
+//    staging) through a buffer resource whose record count ends at the last
+//    key: rows past the end of the sequence arrive as zeros, with no clamp
+//    or branch.  K and V are double-buffered separately, K one tile ahead of
+//    V, so iteration j reads K_{j+1} and V_j while K_{j+2} and V_{j+1} are in
+//    flight.  The LDS tiles are unpadded and XOR-swizzled in 16-byte chunks
+//    so that both the 128-bit K reads and the transposed V reads are free of
+//    bank conflicts.
 //  * exp is v_exp_f32 (2^x) with log2(e) folded into the score scale.
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
@@ -74,6 +83,22 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 // d = 256 the resident Q (64 registers) and O^T (128) leave too little for two.
 template <int D> struct FwdOcc { static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1; };
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// How far ahead the LDS operand reads run: K fragments in k-steps of the score
+// product (three at d = 256, whose 16 k-steps per tile leave more room),
+// V^T fragments in products of P V.
+template <int D> struct FwdPrefetch {
+  static constexpr int K = D == 256 ? 3 : 2;
+  static constexpr int V = 2;
+};
+
 template <typename Tag, int D, bool CAUSAL>
 __global__ void __launch_bounds__(FWD_THREADS, FwdOcc<D>::WAVES_PER_SIMD)
 attn_fwd_kernel(FwdArgs a) {
@@ -87,10 +112,13 @@ attn_fwd_kernel(FwdArgs a) {
   constexpr int NKS = BN / 16;          // k-steps over keys in P V
   static_assert(TILE == 8192 && LPT == 4, "tile shape");
 
-  // Two LDS buffers of [K tile, V tile], as separate objects so the compiler can
-  // tell that the loads in flight into one never alias reads of the other.
-  __shared__ __attribute__((aligned(1024))) uint16_t smem0[2 * TILE];
-  __shared__ __attribute__((aligned(1024))) uint16_t smem1[2 * TILE];
+  // K and V tiles are double-buffered separately: iteration j reads K_{j+1}
+  // and V_j while K_{j+2} and V_{j+1} stream in.  Four separate objects, so
+  // the compiler can tell the loads in flight never alias the reads.
+  __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
+  __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -159,30 +187,24 @@ attn_fwd_kernel(FwdArgs a) {
     ld_koff[i] = (uint32_t)(2 * (r * (int)kv_row + (p ^ swz_k<D>(r)) * 8));
     ld_voff[i] = (uint32_t)(2 * (r * (int)kv_row + (p ^ swz_v<D>(r)) * 8));
   }
-  auto load_tile = [&](int j, uint16_t* kt) {
-    uint16_t* vt = kt + TILE;
-    const size_t tile_off = (size_t)j * BN * kv_row;
-    const char* ksrc = (const char*)(kbase + tile_off);
-    const char* vsrc = (const char*)(vbase + tile_off);
-    if (j * BN + BN <= a.N) {
+  // One tile as a raw buffer resource (stride 0, dword 3 = 0x00020000) whose
+  // record count ends at the sequence end: the per-lane offset is range-
+  // checked, so rows past the end read as zeros (finite, and masked out).
+  auto load_one = [&](int j, const uint16_t* base, const uint32_t* off, uint16_t* dstt) {
+    const uint16_t* src = base + (size_t)j * BN * kv_row;
+    // bytes from the tile's first row to the sequence end: < 2^32, as the host
+    // bounds N * H * d below 2^31 elements
+    const uint32_t nrec = (uint32_t)(a.N - j * BN) * (uint32_t)kv_row * 2u;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)nrec, 0x00020000);
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int dst = (i * FWD_WAVES + wave) * 64 * 8;  // wave-uniform LDS element offset
-        __builtin_amdgcn_global_load_lds((gptr_t)(ksrc + ld_koff[i]), (lptr_t)(kt + dst), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gptr_t)(vsrc + ld_voff[i]), (lptr_t)(vt + dst), 16, 0, 0);
-      }
-    } else {  // the tile runs past the sequence end
-      const int last = a.N - 1 - j * BN;  // last valid row of the tile
-#pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        const int r = ((i * FWD_WAVES + wave) * 64 + lane) / CPR;
-        const uint32_t back = (uint32_t)(2 * max(0, r - last) * (int)kv_row);
-        const int dst = (i * FWD_WAVES + wave) * 64 * 8;
-        __builtin_amdgcn_global_load_lds((gptr_t)(ksrc + (ld_koff[i] - back)), (lptr_t)(kt + dst), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds((gptr_t)(vsrc + (ld_voff[i] - back)), (lptr_t)(vt + dst), 16, 0, 0);
-      }
+    for (int i = 0; i < LPT; ++i) {
+      const int dst = (i * FWD_WAVES + wave) * 64 * 8;  // wave-uniform LDS element offset
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(dstt + dst), 16, off[i], 0, 0, 0);
     }
   };
+  auto load_k = [&](int j, uint16_t* dstt) { load_one(j, kbase, ld_koff, dstt); };
+  auto load_v = [&](int j, uint16_t* dstt) { load_one(j, vbase, ld_voff, dstt); };
 
   // ---- per-lane LDS read offsets (elements, within one tile) ----
   // K (A operand of S^T): row 32 sb + l32, logical chunk 2 kk + half.
@@ -211,140 +233,222 @@ attn_fwd_kernel(FwdArgs a) {
   float m_ref = -INFINITY;  // running max (exp2 domain) the accumulator is scaled to
   float lsum[4] = {0.f, 0.f, 0.f, 0.f};  // this lane's partial row sums (keys of its half)
 
-  auto do_tile = [&](int j, const uint16_t* ks, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const uint16_t* vs = ks + TILE;
-    const int key0 = j * BN;
-    // S^T = K Q^T for this wavefront's 32 queries.  The NSB accumulator chains
-    // advance together one k-step at a time, and the K fragments are read
-    // PF k-steps ahead, so no product waits on its own LDS read.
-    f32x16_t s[NSB];
-    {
-      constexpr int PF = 2;
-      frag8_t kf[PF + 1][NSB];
+  // S^T = K Q^T for one tile into s[], the K fragments read PFK k-steps ahead.
+  // hook(kk) places independent VALU work after k-step kk's products, so that
+  // it issues while they run.
+  auto scores = [&](const uint16_t* ks, f32x16_t* s, auto&& hook) __attribute__((always_inline)) {
+    constexpr int PF = FwdPrefetch<D>::K < NKK ? FwdPrefetch<D>::K : NKK;
+    frag8_t kf[PF + 1][NSB];
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb) s[sb] = (f32x16_t){};
+    for (int sb = 0; sb < NSB; ++sb) s[sb] = (f32x16_t){};
 #pragma unroll
-      for (int kk = 0; kk < PF && kk < NKK; ++kk)
+    for (int kk = 0; kk < PF; ++kk)
 #pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) kf[kk][sb] = *(const frag8_t*)(ks + 32 * sb * D + k_rd[kk]);
-      __builtin_amdgcn_sched_group_barrier(0x100, PF * NSB, 0);  // DS reads
+      for (int sb = 0; sb < NSB; ++sb) kf[kk][sb] = *(const frag8_t*)(ks + 32 * sb * D + k_rd[kk]);
+    static_for<0, NKK>([&](auto kkc) __attribute__((always_inline)) {
+      constexpr int kk = decltype(kkc)::value;
+      if constexpr (kk + PF < NKK) {
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        if (kk + PF < NKK) {
-#pragma unroll
-          for (int sb = 0; sb < NSB; ++sb)
-            kf[(kk + PF) % (PF + 1)][sb] = *(const frag8_t*)(ks + 32 * sb * D + k_rd[kk + PF]);
-        }
-#pragma unroll
-        for (int sb = 0; sb < NSB; ++sb) s[sb] = mfma32(Tag{}, kf[kk % (PF + 1)][sb], qf[kk], s[sb]);
-        if (kk + PF < NKK) __builtin_amdgcn_sched_group_barrier(0x100, NSB, 0);  // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, NSB, 0);                     // MFMA
+        for (int sb = 0; sb < NSB; ++sb)
+          kf[(kk + PF) % (PF + 1)][sb] = *(const frag8_t*)(ks + 32 * sb * D + k_rd[kk + PF]);
       }
-    }
-    if (MASK) {
 #pragma unroll
-      for (int sb = 0; sb < NSB; ++sb)
+      for (int sb = 0; sb < NSB; ++sb) s[sb] = mfma32(Tag{}, kf[kk % (PF + 1)][sb], qf[kk], s[sb]);
+      hook(kkc);
+    });
+  };
+
+  // Softmax of the current tile's scores, split in pieces that fill the
+  // shadow of the next tile's score products: the row max over the first half
+  // of the k-steps, then the probabilities of the first half of the key
+  // k-steps over the second half.  The rest of P is formed inside P V.
+  struct SoftState {
+    float mx4[4];
+    float nm;          // -(reference max the tile's P is scaled to)
+    float m_new;
+    bool need;         // wave-uniform: the reference max moves this tile
+    float tsum[4];     // this tile's partial row sums
+    uint32_t w[NKS][4];
+  };
+
+  auto row_max_part = [&](const f32x16_t* s, SoftState& st, int e0, int e1) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool ok = key < a.N && (!CAUSAL || key <= qrow);
-          s[sb][r] = ok ? s[sb][r] : -INFINITY;
-        }
+    for (int e = e0; e < e1; e += 2) {
+      const int sb = e / 16, r = e % 16;
+      st.mx4[(e >> 1) & 3] = fmaxf(st.mx4[(e >> 1) & 3], fmaxf(s[sb][r], s[sb][r + 1]));
     }
-    // row max: four independent v_max3 chains, then one exchange between the halves
-    float mx4[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  };
+  auto row_max_end = [&](SoftState& st) __attribute__((always_inline)) {
+    float mx = fmaxf(fmaxf(st.mx4[0], st.mx4[1]), fmaxf(st.mx4[2], st.mx4[3]));
+    const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
+                                                     __builtin_bit_cast(uint32_t, mx), false, false);
+    mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
+    const float mxs = mx * c;
+    // deferred rescale: move the reference max only when it grows by > 2^8
+    st.need = __builtin_amdgcn_ballot_w64(mxs > m_ref + RESCALE_THRESHOLD) != 0;
+    st.m_new = st.need ? fmaxf(m_ref, mxs) : m_ref;
+    st.nm = -st.m_new;
+  };
+  // probability pairs [p0, p1) of the tile, pair index = 4 * key-k-step + t
+  auto probs = [&](const f32x16_t* s, SoftState& st, int p0, int p1, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+    for (int pp = p0; pp < p1; ++pp) {
+      const int f = pp / 4, t = pp % 4;
+      const int sb = f / 2, r = 8 * (f % 2) + 2 * t;
+      float e0 = fast_exp2(__builtin_fmaf(s[sb][r], c, st.nm));
+      float e1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], c, st.nm));
+      if (MASK) {  // exp2(-inf * 0) would be NaN when scale == 0
+        e0 = s[sb][r] == -INFINITY ? 0.f : e0;
+        e1 = s[sb][r + 1] == -INFINITY ? 0.f : e1;
+      }
+      st.w[f][t] = pack2(Tag{}, e0, e1);
+      st.tsum[t] += e0 + e1;  // fp32 row sum: LSE must not carry 16-bit rounding
+      asm volatile("" : "+v"(st.w[f][t]), "+v"(st.tsum[t]));  // formed here, not sunk to its use
+    }
+  };
+  auto soft_init = [&](SoftState& st) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      st.mx4[t] = -INFINITY;
+      st.tsum[t] = 0.f;
+    }
+  };
+  auto apply_mask = [&](f32x16_t* s, int j) __attribute__((always_inline)) {
+    const int key0 = j * BN;
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
-      for (int r = 0; r < 16; r += 2)
-        mx4[(r >> 1) & 3] = fmaxf(mx4[(r >> 1) & 3], fmaxf(s[sb][r], s[sb][r + 1]));
-    float mx = fmaxf(fmaxf(mx4[0], mx4[1]), fmaxf(mx4[2], mx4[3]));
-    {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
-                                                       __builtin_bit_cast(uint32_t, mx), false, false);
-      mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
-    }
-    const float mxs = mx * c;
-    // deferred rescale: move the reference max only when it grows by > 2^8
-    if (__builtin_amdgcn_ballot_w64(mxs > m_ref + RESCALE_THRESHOLD) != 0) {
-      const float m_new = fmaxf(m_ref, mxs);
-      const float alpha = fast_exp2(m_ref - m_new);
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool ok = key < a.N && (!CAUSAL || key <= qrow);
+        s[sb][r] = ok ? s[sb][r] : -INFINITY;
+      }
+  };
+  // move the reference max (rare) -- after the probabilities, before P V
+  auto rescale = [&](SoftState& st) __attribute__((always_inline)) {
+    if (st.need) {
+      const float alpha = fast_exp2(m_ref - st.m_new);
 #pragma unroll
       for (int t = 0; t < 4; ++t) lsum[t] *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-      m_ref = m_new;
     }
-    // P = 2^(s*c - m_ref), rounded to 16 bits: the B operand of O^T += V^T P^T
-    const float nm = -m_ref;
-    frag8_t pf[NKS];
+    m_ref = st.m_new;
+  };
+  // O^T += V^T P^T, the second half of P formed in the shadow of the first
+  // half's products; V^T fragments read PFV products ahead.
+  auto pv = [&](const uint16_t* vs, const f32x16_t* s, SoftState& st, auto mask_tag) __attribute__((always_inline)) {
+    constexpr int NF = NKS * NDB;
+    constexpr int PFV = FwdPrefetch<D>::V;
+    constexpr int PAIRS2 = (NKS / 2) * 4;        // pairs still to form
+    constexpr int NM2 = (NKS / 2) * NDB;         // products they may hide under
+    frag8_t vf[PFV + 1];
+    auto rd = [&](int f) __attribute__((always_inline)) {
+      const uint16_t* p = vs + 16 * (f / NDB) * D + v_rd[f % NDB];
+      s16x4_t lo = lds_read_tr(p);
+      s16x4_t hi = lds_read_tr(p + 8 * D);
+      return (frag8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
 #pragma unroll
-    for (int sb = 0; sb < NSB; ++sb) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        uint32_t w[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int r = 8 * hh + 2 * t;
-          float p0 = fast_exp2(__builtin_fmaf(s[sb][r], c, nm));
-          float p1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], c, nm));
-          if (MASK) {  // exp2(-inf * 0) would be NaN when scale == 0
-            p0 = s[sb][r] == -INFINITY ? 0.f : p0;
-            p1 = s[sb][r + 1] == -INFINITY ? 0.f : p1;
-          }
-          w[t] = pack2(Tag{}, p0, p1);
-          lsum[t] += p0 + p1;  // fp32 row sum: LSE must not carry 16-bit rounding
-        }
-        u32x4_t wv = {w[0], w[1], w[2], w[3]};
-        pf[2 * sb + hh] = __builtin_bit_cast(frag8_t, wv);
+    for (int f = 0; f < PFV; ++f) vf[f] = rd(f);
+    static_for<0, NF>([&](auto fc) __attribute__((always_inline)) {
+      constexpr int f = decltype(fc)::value;
+      if constexpr (f + PFV < NF) vf[(f + PFV) % (PFV + 1)] = rd(f + PFV);
+      constexpr int ks = f / NDB, db = f % NDB;
+      if constexpr (f < NM2) {  // pairs [PAIRS2 * f / NM2, PAIRS2 * (f + 1) / NM2) of the second half
+        constexpr int q0 = PAIRS2 * f / NM2, q1 = PAIRS2 * (f + 1) / NM2;
+        probs(s, st, (NKS / 2) * 4 + q0, (NKS / 2) * 4 + q1, mask_tag);
       }
-    }
-    // O^T += V^T P^T : A operand V^T via transposed LDS reads
+      const u32x4_t wv = {st.w[ks][0], st.w[ks][1], st.w[ks][2], st.w[ks][3]};
+      oacc[db] = mfma32(Tag{}, vf[f % (PFV + 1)], __builtin_bit_cast(frag8_t, wv), oacc[db]);
+    });
 #pragma unroll
-    for (int ksb = 0; ksb < NKS; ++ksb) {
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const uint16_t* p = vs + 16 * ksb * D + v_rd[db];
-        s16x4_t lo = lds_read_tr(p);
-        s16x4_t hi = lds_read_tr(p + 8 * D);
-        frag8_t vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        oacc[db] = mfma32(Tag{}, vf, pf[ksb], oacc[db]);
-      }
-    }
+    for (int t = 0; t < 4; ++t) lsum[t] += st.tsum[t];
   };
 
-  uint16_t* const buf0 = smem0;
-  uint16_t* const buf1 = smem1;
-  load_tile(0, buf0);
+  // One pipelined step: softmax and P V of tile j (scores in s_cur) with the
+  // next tile's scores formed in between.  HAS_NEXT false: no next scores.
+  auto step = [&](int j, const uint16_t* knext, const uint16_t* vcur, f32x16_t* s_cur, f32x16_t* s_next,
+                  auto mask_tag, auto next_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    constexpr bool HAS_NEXT = decltype(next_tag)::value;
+    SoftState st;
+    soft_init(st);
+    if (MASK) apply_mask(s_cur, j);
+    constexpr int H = NKK / 2 > 0 ? NKK / 2 : 1;   // k-steps for the row max
+    constexpr int NE = NSB * 16;                   // score elements per lane
+    constexpr int PAIRS1 = (NKS / 2) * 4;          // probability pairs in the first half
+    constexpr int H2 = NKK - H;                    // k-steps for them
+    auto hook = [&](auto kkc) __attribute__((always_inline)) {
+      constexpr int kk = decltype(kkc)::value;
+      if constexpr (kk < H) {
+        row_max_part(s_cur, st, NE * kk / H, NE * (kk + 1) / H);
+        if constexpr (kk == H - 1) row_max_end(st);
+      } else {
+        constexpr int i = kk - H;
+        probs(s_cur, st, PAIRS1 * i / H2, PAIRS1 * (i + 1) / H2, mask_tag);
+      }
+    };
+    if constexpr (HAS_NEXT) {
+      scores(knext, s_next, hook);
+    } else {
+      static_for<0, NKK>(hook);
+    }
+    rescale(st);
+    pv(vcur, s_cur, st, mask_tag);
+  };
+
+  f32x16_t sA[NSB], sB[NSB];
+  uint16_t* const kb0 = k0s;
+  uint16_t* const kb1 = k1s;
+  uint16_t* const vb0 = v0s;
+  uint16_t* const vb1 = v1s;
+
+  // prologue: K_0, V_0, K_1 resident; scores of tile 0
+  load_k(0, kb0);
+  load_v(0, vb0);
+  if (1 < ntiles) load_k(1, kb1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  scores(kb0, sA, [](auto) {});
+  __syncthreads();  // every wavefront is done with K_0 before K_2 replaces it
 
-  // One barrier per tile: every wavefront passes exactly `ntiles` barriers,
-  // whichever loop it spends them in.  Tile j lives in buffer j & 1; the
-  // steady-state loop takes tiles in pairs so both buffer offsets are constants.
-  auto step = [&](int j, uint16_t* cur, uint16_t* nxt, auto mask_tag) {
-    if (j + 1 < ntiles) load_tile(j + 1, nxt);
-    do_tile(j, cur, mask_tag);
+  // Iteration j: loads K_{j+2} -> K buffer j & 1 and V_{j+1} -> V buffer
+  // (j + 1) & 1, reads K_{j+1} and V_j, one barrier at its end.  Every
+  // wavefront passes exactly `ntiles` of these barriers.
+  auto iter_loads = [&](int j, uint16_t* kdst, uint16_t* vdst) __attribute__((always_inline)) {
+    if (j + 2 < ntiles) load_k(j + 2, kdst);
+    if (j + 1 < ntiles) load_v(j + 1, vdst);
+  };
+  auto iter_end = [&]() __attribute__((always_inline)) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
   int j = 0;
-  for (; j + 1 < nfull; j += 2) {  // steady state: no element mask
-    step(j, buf0, buf1, std::false_type{});
-    step(j + 1, buf1, buf0, std::false_type{});
+  // steady state: tile j unmasked and tile j + 1 computed by this wavefront
+  for (; j + 2 < nfull; j += 2) {
+    iter_loads(j, kb0, vb1);
+    step(j, kb1, vb0, sA, sB, std::false_type{}, std::true_type{});
+    iter_end();
+    iter_loads(j + 1, kb1, vb0);
+    step(j + 1, kb0, vb1, sB, sA, std::false_type{}, std::true_type{});
+    iter_end();
   }
-  if (j < nfull) {
-    step(j, buf0, buf1, std::false_type{});
-    ++j;
-  }
-  for (; j < ntiles; ++j) {  // diagonal / ragged tiles, then tiles only other wavefronts need
-    uint16_t* cur = (j & 1) ? buf1 : buf0;
-    uint16_t* nxt = (j & 1) ? buf0 : buf1;
-    if (j + 1 < ntiles) load_tile(j + 1, nxt);
-    if (j < nwave) do_tile(j, cur, std::true_type{});
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  // remaining tiles: the diagonal / ragged ones, the last unmasked ones, and
+  // tiles only other wavefronts need.  Not overlapped: the next tile's scores
+  // are formed after this one's P V, in the same registers.
+  for (; j < ntiles; ++j) {
+    uint16_t* kcur = (j & 1) ? kb1 : kb0;   // K buffer j & 1 receives K_{j+2}
+    uint16_t* knext = (j & 1) ? kb0 : kb1;
+    uint16_t* vcur = (j & 1) ? vb1 : vb0;
+    uint16_t* vnext = (j & 1) ? vb0 : vb1;
+    iter_loads(j, kcur, vnext);
+    if (j < nwave) {
+      step(j, knext, vcur, sA, sB, std::true_type{}, std::false_type{});
+      if (j + 1 < nwave) scores(knext, sA, [](auto) {});
+    }
+    iter_end();
   }
 
   // ---- epilogue: one division per row, LSE in natural log ----
