@@ -6,8 +6,9 @@
 //    result is folded into the output (FlashAttention-2 announcement, "具体实现"
 //    section; FlashAttention-1 news page, "FlashAttention" section).
 //  * Parallel over sequence length: one workgroup per (batch, query head,
-//    block of 128 query rows), so the grid fills 256 CUs even for small
-//    batch * heads (announcement, "具体实现"; review, "Параллелизм").
+//    block of 256 query rows, 128 when causal or at d = 256), so the grid
+//    fills 256 CUs even for small batch * heads (announcement, "具体实现";
+//    review, "Параллелизм").
 //  * Work split inside a workgroup: each 64-lane wavefront owns 32 query rows
 //    and all wavefronts share the K/V tiles, so wavefronts never exchange
 //    partial outputs (announcement, "具体实现": Q split across warps, K/V
@@ -24,8 +25,10 @@
 //    "Алгоритм вычисления").
 //
 // CDNA4 mapping.
-//  * Occupancy: two workgroups of four wavefronts per CU (two wavefronts per
-//    SIMD, <= 256 registers each).
+//  * Occupancy: two wavefronts per SIMD (<= 256 registers each) at d <= 128:
+//    one workgroup of eight wavefronts per CU when non-causal, so a K/V tile
+//    staged in LDS serves 256 query rows, or two workgroups of four when
+//    causal.  At d = 256 one wavefront per SIMD.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 //    accumulator holds one query per lane and 16 keys per register block, so
 //    the row max / row sum are in-lane except one v_permlane32_swap between
@@ -55,9 +58,16 @@ namespace attn {
 
 namespace {
 
-constexpr int FWD_BM = 128;     // query rows per workgroup
-constexpr int FWD_WAVES = 4;    // 32 query rows per wavefront
-constexpr int FWD_THREADS = FWD_WAVES * 64;
+// Wavefronts per workgroup (32 query rows each).  Non-causal at d <= 128:
+// eight, one workgroup per CU at two wavefronts per SIMD, so each K/V tile is
+// staged once per 256 query rows.  Causal: four, since the wavefronts of a
+// diagonal block have unequal trip counts and wait for the longest at every
+// barrier.  d = 256: four (one wavefront per SIMD).
+template <int D, bool CAUSAL> struct FwdWG {
+  static constexpr int WAVES = (D <= 128 && !CAUSAL) ? 8 : 4;
+  static constexpr int THREADS = WAVES * 64;
+  static constexpr int BM = WAVES * 32;
+};
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units: rescale only if the max grows > 2^8
 
 // Key-tile height per head dimension: every K or V tile is 16 KiB.
@@ -81,7 +91,10 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Wavefronts per SIMD the register budget is cut for: two for d <= 128; at
 // d = 256 the resident Q (64 registers) and O^T (128) leave too little for two.
-template <int D> struct FwdOcc { static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1; };
+template <int D, bool CAUSAL> struct FwdOcc {
+  static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1;
+  static constexpr int MIN_WG_PER_CU = WAVES_PER_SIMD * 4 / FwdWG<D, CAUSAL>::WAVES;  // launch-bounds form
+};
 
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -100,17 +113,19 @@ template <int D> struct FwdPrefetch {
 };
 
 template <typename Tag, int D, bool CAUSAL>
-__global__ void __launch_bounds__(FWD_THREADS, FwdOcc<D>::WAVES_PER_SIMD)
+__global__ void __launch_bounds__((FwdWG<D, CAUSAL>::THREADS), (FwdOcc<D, CAUSAL>::MIN_WG_PER_CU))
 attn_fwd_kernel(FwdArgs a) {
   constexpr int BN = FwdTile<D>::BN;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILE = BN * D;          // elements per K or V tile (8192)
-  constexpr int LPT = TILE / 8 / FWD_THREADS;  // 16-byte loads per thread per tensor (4)
+  constexpr int FWD_WAVES = FwdWG<D, CAUSAL>::WAVES;
+  constexpr int FWD_BM = FwdWG<D, CAUSAL>::BM;
+  constexpr int LPT = TILE / 8 / FwdWG<D, CAUSAL>::THREADS;  // 16-byte loads per thread per tensor
   constexpr int NKK = D / 16;           // MFMA k-steps over d
   constexpr int NSB = BN / 32;          // 32-key sub-blocks per tile
   constexpr int NDB = D / 32;           // 32-wide d blocks of O
   constexpr int NKS = BN / 16;          // k-steps over keys in P V
-  static_assert(TILE == 8192 && LPT == 4, "tile shape");
+  static_assert(TILE == 8192 && LPT * 8 * FwdWG<D, CAUSAL>::THREADS == TILE, "tile shape");
 
   // K and V tiles are double-buffered separately: iteration j reads K_{j+1}
   // and V_j while K_{j+2} and V_{j+1} stream in.  Four separate objects, so
@@ -482,10 +497,10 @@ attn_fwd_kernel(FwdArgs a) {
 
 template <typename Tag, int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  const int nblk = (a.N + FWD_BM - 1) / FWD_BM;
+  const int nblk = (a.N + FwdWG<D, CAUSAL>::BM - 1) / FwdWG<D, CAUSAL>::BM;
   const long long total = (long long)nblk * a.Hq * a.B;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL>), dim3((unsigned)total), dim3(FWD_THREADS),
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL>), dim3((unsigned)total), dim3(FwdWG<D, CAUSAL>::THREADS),
                      0, stream, a);
   return hipGetLastError();
 }
