@@ -28,14 +28,17 @@
 // deterministic.
 //
 // CDNA4 mapping (v_mfma_f32_32x32x16, 64-lane wavefronts, two wavefronts per
-// SIMD for d <= 128).  Tiles move HBM -> LDS by global_load_lds_dwordx4 into
-// unpadded tiles swizzled in 16-byte chunks; the swizzle is free of bank
+// SIMD for d <= 128).  Tiles move HBM -> LDS by DMA (buffer_load_dwordx4 ...
+// lds for dK/dV, global_load_lds_dwordx4 for dQ) into unpadded tiles
+// swizzled in 16-byte chunks; the swizzle is free of bank
 // conflicts both for 128-bit row reads (16 rows x one chunk per cycle) and
 // for ds_read_b64_tr_b16 transposed reads (4 rows x 4 chunks per cycle),
 // because every tile here is read both ways.
 //  * dK/dV: S = Q K^T and dP = dO V^T with the key on the lane, so P and dS
 //    are directly the B operands of dV^T += dO^T P and dK^T += Q^T dS; dO^T
-//    and Q^T are transposed reads of the Q / dO tiles.
+//    and Q^T are transposed reads of the Q / dO tiles.  The operand
+//    fragments of every product are read one k-step (S, dP) or two products
+//    (dV, dK) ahead of their use, so a product rarely waits on LDS latency.
 //  * dQ: S^T = K Q^T and dP^T = V dO^T with the query on the lane (LSE and D
 //    are per lane), so dS^T is directly the B operand of dQ^T += K^T dS^T;
 //    K^T is a transposed read of the K tile.
@@ -70,9 +73,27 @@ __device__ __forceinline__ void wait_loads() { asm volatile("s_waitcnt vmcnt(0)"
 // HBM -> LDS load of a tile of R rows x D columns (16-bit) with the swizzle,
 // shared by the W wavefronts of a workgroup.  Thread (wave, lane) fills chunks
 // (W i + wave) * 64 + lane; when the tile has fewer chunks than threads, the
-// wavefronts past its end load nothing.  Rows at or past `valid` read row valid - 1 instead
+// wavefronts past its end load nothing.
+//
+// Two forms.  The buffer form (buffer_load_dwordx4 ... lds; the dK/dV pass)
+// leaves the LDS wait counter usable: the compiler counts global_load_lds as
+// an LDS access that may complete out of order and so waits for every
+// outstanding LDS read (lgkmcnt(0)) before each product while a tile load is
+// in flight, which serialised the dK/dV products on LDS latency (11% of its
+// time).  The dQ pass, whose products wait less on LDS, measured within a
+// few percent either way and keeps the global form (GLOBAL_DMA).  Rows at or past `valid` read row valid - 1 instead
 // (any finite values do: they are masked or never stored).
-template <int D, int R, int W = 4>
+// One 16-byte-per-lane HBM -> LDS load through a raw buffer resource
+// (stride 0, dword 3 = 0x00020000) of nrec bytes from base: lanes whose offset
+// is past the record count write zeros.  (A free function: with the resource
+// built inside a member of a class template, this compiler silently dropped
+// the host-side launch stubs of some kernel instantiations.)
+__device__ __forceinline__ void buffer_lds16(const void* base, uint32_t nrec, uint32_t voff, uint16_t* dst) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)nrec, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)dst, 16, voff, 0, 0, 0);
+}
+
+template <int D, int R, int W = 4, bool GLOBAL_DMA = false>
 struct TileDma {
   static constexpr int CPR = D / 8;
   static constexpr int CHUNKS = R * CPR;
@@ -93,24 +114,33 @@ struct TileDma {
       off[i] = (uint32_t)(2 * (r * gstride + (p ^ swz<D>(r)) * 8));
     }
   }
-  // src: first row of the tile; valid: rows of the tile that exist.
+  // src: first row of the tile; valid: rows of the tile that exist.  Rows at
+  // or past `valid` read as zeros (buffer form: the record count ends there)
+  // or as row valid - 1 (global form); any finite values do, since their
+  // probabilities are masked to 0.
   __device__ __forceinline__ void load(const uint16_t* src, int valid, int gstride, uint16_t* dst) const {
-    const char* s = (const char*)src;
-    if (valid >= R) {
+    if (GLOBAL_DMA) {
+      const char* s = (const char*)src;
+      if (valid >= R) {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i)
-        if (has(i))
-          __builtin_amdgcn_global_load_lds((gptr_t)(s + off[i]), (lptr_t)(dst + (i * W + wave) * 512), 16, 0, 0);
-    } else {
+        for (int i = 0; i < LPT; ++i)
+          if (has(i))
+            __builtin_amdgcn_global_load_lds((gptr_t)(s + off[i]), (lptr_t)(dst + (i * W + wave) * 512), 16, 0, 0);
+      } else {
 #pragma unroll
-      for (int i = 0; i < LPT; ++i) {
-        if (!has(i)) continue;
-        const int r = ((i * W + wave) * 64 + lane) / CPR;
-        const uint32_t back = (uint32_t)(2 * max(0, r - (valid - 1)) * gstride);
-        __builtin_amdgcn_global_load_lds((gptr_t)(s + (off[i] - back)),
-                                         (lptr_t)(dst + (i * W + wave) * 512), 16, 0, 0);
+        for (int i = 0; i < LPT; ++i) {
+          if (!has(i)) continue;
+          const int r = ((i * W + wave) * 64 + lane) / CPR;
+          const uint32_t back = (uint32_t)(2 * max(0, r - (valid - 1)) * gstride);
+          __builtin_amdgcn_global_load_lds((gptr_t)(s + (off[i] - back)), (lptr_t)(dst + (i * W + wave) * 512), 16, 0, 0);
+        }
       }
+      return;
     }
+    const uint32_t nrec = (uint32_t)(valid < R ? valid : R) * (uint32_t)gstride * 2u;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i)
+      if (has(i)) buffer_lds16(src, nrec, off[i], dst + (i * W + wave) * 512);
   }
 };
 
@@ -209,6 +239,7 @@ template <int D, int W> struct BwdBounds {
 // 2. dK, dV: one workgroup per (batch, K/V head, 128 keys)
 // ---------------------------------------------------------------------------
 constexpr int KV_BM = 32;   // query rows per tile
+constexpr int BWD_PFT = 2;  // transposed fragments read ahead in dV/dK
 
 template <typename Tag, int D, bool CAUSAL>
 __global__ void __launch_bounds__((BwdBounds<D, DkdvWG<D, CAUSAL>::WAVES>::THREADS),
@@ -327,13 +358,27 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     int h, q0;
     coords(t, h, q0);
     (void)h;
-    // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys
+    // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys;
+    // the Q, dO (and V) fragments of k-step kk + 1 are read while k-step kk's
+    // two products run
     f32x16_t s = {}, dp = {};
+    {
+      frag8_t qa[2], oa[2], va[2];
+      auto rd = [&](int kk, int i) __attribute__((always_inline)) {
+        qa[i] = fr.row(qs, 0, kk);
+        oa[i] = fr.row(os, 0, kk);
+        if (V_LDS) va[i] = fr.row(vblk, wave, kk);
+      };
+      rd(0, 0);
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      s = mfma32(Tag{}, fr.row(qs, 0, kk), kf[kk], s);
-      const frag8_t vv = V_LDS ? fr.row(vblk, wave, kk) : vf[V_LDS ? 0 : kk];
-      dp = mfma32(Tag{}, fr.row(os, 0, kk), vv, dp);
+      for (int kk = 0; kk < NKK; ++kk) {
+        if (kk + 1 < NKK) rd(kk + 1, (kk + 1) & 1);
+        s = mfma32(Tag{}, qa[kk & 1], kf[kk], s);
+        const frag8_t vv = V_LDS ? va[kk & 1] : vf[V_LDS ? 0 : kk];
+        dp = mfma32(Tag{}, oa[kk & 1], vv, dp);
+        if (kk + 1 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, V_LDS ? 3 : 2, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                // MFMA
+      }
     }
     // P = 2^(S c - LSE2), dS = P (dP - D); C rows = queries 8 (r / 4) + 4 half + r % 4
     const int klim = mykey - q0 - 4 * half;
@@ -356,17 +401,31 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
       dsw[2 * r4] = pack2(Tag{}, dsv[0], dsv[1]);
       dsw[2 * r4 + 1] = pack2(Tag{}, dsv[2], dsv[3]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries (two k-steps)
+    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries (two
+    // k-steps); the transposed fragments are read PFT products ahead
+    {
+      constexpr int NF = 2 * 2 * NDB;  // products, in (ks, db, dV/dK) order
+      constexpr int PFT = BWD_PFT;
+      frag8_t ta[PFT + 1];
+      auto rd = [&](int f) __attribute__((always_inline)) {
+        const int ks = f / (2 * NDB), db = (f / 2) % NDB;
+        return fr.tr((f & 1) ? qs : os, ks, db);
+      };
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const u32x4_t p4 = {pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]};
-      const u32x4_t d4 = {dsw[4 * ks], dsw[4 * ks + 1], dsw[4 * ks + 2], dsw[4 * ks + 3]};
-      const frag8_t pfrag = __builtin_bit_cast(frag8_t, p4);
-      const frag8_t dsfrag = __builtin_bit_cast(frag8_t, d4);
+      for (int f = 0; f < PFT; ++f) ta[f] = rd(f);
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        dv_acc[db] = mfma32(Tag{}, fr.tr(os, ks, db), pfrag, dv_acc[db]);
-        dk_acc[db] = mfma32(Tag{}, fr.tr(qs, ks, db), dsfrag, dk_acc[db]);
+      for (int f = 0; f < NF; ++f) {
+        if (f + PFT < NF) ta[(f + PFT) % (PFT + 1)] = rd(f + PFT);
+        const int ks = f / (2 * NDB), db = (f / 2) % NDB;
+        if (f & 1) {
+          const u32x4_t d4 = {dsw[4 * ks], dsw[4 * ks + 1], dsw[4 * ks + 2], dsw[4 * ks + 3]};
+          dk_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, d4), dk_acc[db]);
+        } else {
+          const u32x4_t p4 = {pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]};
+          dv_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, p4), dv_acc[db]);
+        }
+        if (f + PFT < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
       }
     }
   };
@@ -489,7 +548,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
 
   const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.N * a.Hkv + g) * D;
   const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.N * a.Hkv + g) * D;
-  TileDma<D, BN, W> dma;
+  TileDma<D, BN, W, true> dma;
   dma.init(kv_row, wave, lane);
   FragRd<D> fr;
   fr.init(lane);
