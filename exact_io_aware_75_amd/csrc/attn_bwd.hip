@@ -41,7 +41,8 @@
 //    (dV, dK) ahead of their use, so a product rarely waits on LDS latency.
 //  * dQ: S^T = K Q^T and dP^T = V dO^T with the query on the lane (LSE and D
 //    are per lane), so dS^T is directly the B operand of dQ^T += K^T dS^T;
-//    K^T is a transposed read of the K tile.
+//    K^T is a transposed read of the K tile.  Operand fragments are read one
+//    k-step (S^T, dP^T) or two products (dQ^T) ahead, as in dK/dV.
 #include "attn_common.hpp"
 #include "attn_kernels.hpp"
 
@@ -587,10 +588,21 @@ attn_bwd_dq_kernel(BwdArgs a) {
     for (int sb = 0; sb < NSB; ++sb) {
       frag8_t dsf[2];
       f32x16_t s = {}, dp = {};
+      {  // K and V fragments of k-step kk + 1 are read while k-step kk's products run
+        frag8_t ka[2], va[2];
+        ka[0] = fr.row(ks, sb, 0);
+        va[0] = fr.row(vs, sb, 0);
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        s = mfma32(Tag{}, fr.row(ks, sb, kk), qf[kk], s);
-        dp = mfma32(Tag{}, fr.row(vs, sb, kk), of[kk], dp);
+        for (int kk = 0; kk < NKK; ++kk) {
+          if (kk + 1 < NKK) {
+            ka[(kk + 1) & 1] = fr.row(ks, sb, kk + 1);
+            va[(kk + 1) & 1] = fr.row(vs, sb, kk + 1);
+          }
+          s = mfma32(Tag{}, ka[kk & 1], qf[kk], s);
+          dp = mfma32(Tag{}, va[kk & 1], of[kk], dp);
+          if (kk + 1 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                    // MFMA
+        }
       }
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
@@ -610,12 +622,21 @@ attn_bwd_dq_kernel(BwdArgs a) {
         dsf[hh] = __builtin_bit_cast(frag8_t, wv);
       }
       // dQ^T += K^T dS^T over the sub-block's 32 keys: A operand K^T via
-      // transposed reads of the K tile
+      // transposed reads of the K tile, two products ahead
+      {
+        constexpr int NF = 2 * NDB;
+        constexpr int PFT = 2;
+        frag8_t ta[PFT + 1];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+        for (int f = 0; f < PFT; ++f) ta[f] = fr.tr(ks, 2 * sb + f / NDB, f % NDB);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-          dq_acc[db] = mfma32(Tag{}, fr.tr(ks, 2 * sb + hh, db), dsf[hh], dq_acc[db]);
+        for (int f = 0; f < NF; ++f) {
+          if (f + PFT < NF) ta[(f + PFT) % (PFT + 1)] = fr.tr(ks, 2 * sb + (f + PFT) / NDB, (f + PFT) % NDB);
+          dq_acc[f % NDB] = mfma32(Tag{}, ta[f % (PFT + 1)], dsf[f / NDB], dq_acc[f % NDB]);
+          if (f + PFT < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+        }
+      }
     }
   };
 
