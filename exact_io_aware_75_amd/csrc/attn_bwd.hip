@@ -149,36 +149,34 @@ struct TileDma {
 // swizzled tile whose row stride is D elements.
 template <int D>
 struct FragRd {
+  // Per-lane base element offsets.  The swizzled chunk bits of every offset
+  // lie below the row bits, so the offset of k-step kk (or d block db) is the
+  // base XOR a constant: one v_xor per read instead of a shift, XOR and add.
   // 128-bit row reads: row = 32-aligned base + l32, logical chunk 2 kk + half.
-  int row_off, row_x;
+  int row_b;
   // transposed reads: rows 16 ks + {0, 8} + 4 half + gi / 4, elements
   // 32 db + 16 (grp & 1) + 4 (gi & 3).
-  int tr_lo, tr_hi, x_lo, x_hi;
+  int tr_lo, tr_hi;
   __device__ __forceinline__ void init(int lane) {
     const int half = lane >> 5, l32 = lane & 31, grp = lane >> 4, gi = lane & 15;
-    row_off = l32 * D;
-    row_x = swz<D>(l32) ^ half;
+    row_b = l32 * D + ((swz<D>(l32) ^ half) << 3);
     const int r = 4 * half + (gi >> 2);
     const int cl = 2 * (grp & 1) + ((gi & 3) >> 1);
-    tr_lo = r * D + 4 * (gi & 1);
-    tr_hi = (r + 8) * D + 4 * (gi & 1);
-    x_lo = swz<D>(r) ^ cl;
-    x_hi = swz<D>(r + 8) ^ cl;
+    tr_lo = r * D + 4 * (gi & 1) + ((swz<D>(r) ^ cl) << 3);
+    tr_hi = (r + 8) * D + 4 * (gi & 1) + ((swz<D>(r + 8) ^ cl) << 3);
   }
   // Hide the offsets from loop-invariant code motion (which would otherwise
   // keep one copy of every address per LDS buffer live across the loop).
-  __device__ __forceinline__ void pin() {
-    asm volatile("" : "+v"(row_off), "+v"(row_x), "+v"(tr_lo), "+v"(tr_hi), "+v"(x_lo), "+v"(x_hi));
-  }
+  __device__ __forceinline__ void pin() { asm volatile("" : "+v"(row_b), "+v"(tr_lo), "+v"(tr_hi)); }
   // fragment of rows [32 rb, 32 rb + 32), k-step kk (16 columns)
   __device__ __forceinline__ frag8_t row(const uint16_t* t, int rb, int kk) const {
-    return *(const frag8_t*)(t + 32 * rb * D + row_off + (((2 * kk) ^ row_x) << 3));
+    return *(const frag8_t*)(t + 32 * rb * D + (row_b ^ (16 * kk)));
   }
   // transposed fragment: reduction rows [16 ks, 16 ks + 16), columns [32 db, 32 db + 32)
   __device__ __forceinline__ frag8_t tr(const uint16_t* t, int ks, int db) const {
     const uint16_t* base = t + 16 * ks * D;
-    const s16x4_t lo = lds_read_tr(base + tr_lo + (((4 * db) ^ x_lo) << 3));
-    const s16x4_t hi = lds_read_tr(base + tr_hi + (((4 * db) ^ x_hi) << 3));
+    const s16x4_t lo = lds_read_tr(base + (tr_lo ^ (32 * db)));
+    const s16x4_t hi = lds_read_tr(base + (tr_hi ^ (32 * db)));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
 };
@@ -383,7 +381,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     }
     // P = 2^(S c - LSE2), dS = P (dP - D); C rows = queries 8 (r / 4) + 4 half + r % 4
     const int klim = mykey - q0 - 4 * half;
-    uint32_t pw[8], dsw[8];
+    u32x4_t pq[2], dsq[2];  // packed P and dS, already the B-operand register tuples
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const f32x4_t l4 = *(const f32x4_t*)(ls + 8 * r4 + 4 * half);
@@ -397,10 +395,10 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         p[e] = pv;
         dsv[e] = pv * (dp[r] - d4[e]);
       }
-      pw[2 * r4] = pack2(Tag{}, p[0], p[1]);
-      pw[2 * r4 + 1] = pack2(Tag{}, p[2], p[3]);
-      dsw[2 * r4] = pack2(Tag{}, dsv[0], dsv[1]);
-      dsw[2 * r4 + 1] = pack2(Tag{}, dsv[2], dsv[3]);
+      pq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, p[0], p[1]);
+      pq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, p[2], p[3]);
+      dsq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, dsv[0], dsv[1]);
+      dsq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, dsv[2], dsv[3]);
     }
     // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries (two
     // k-steps); the transposed fragments are read PFT products ahead
@@ -418,13 +416,10 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
       for (int f = 0; f < NF; ++f) {
         if (f + PFT < NF) ta[(f + PFT) % (PFT + 1)] = rd(f + PFT);
         const int ks = f / (2 * NDB), db = (f / 2) % NDB;
-        if (f & 1) {
-          const u32x4_t d4 = {dsw[4 * ks], dsw[4 * ks + 1], dsw[4 * ks + 2], dsw[4 * ks + 3]};
-          dk_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, d4), dk_acc[db]);
-        } else {
-          const u32x4_t p4 = {pw[4 * ks], pw[4 * ks + 1], pw[4 * ks + 2], pw[4 * ks + 3]};
-          dv_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, p4), dv_acc[db]);
-        }
+        if (f & 1)
+          dk_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, dsq[ks]), dk_acc[db]);
+        else
+          dv_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, pq[ks]), dv_acc[db]);
         if (f + PFT < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
       }
