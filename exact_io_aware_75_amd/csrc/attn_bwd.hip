@@ -51,6 +51,7 @@ namespace attn {
 namespace {
 
 typedef __attribute__((address_space(1))) const void* gptr_t;
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lptr_t;
 
 // 16-byte-chunk swizzle (row r, logical chunk c stored at chunk c ^ swz(r));
@@ -252,6 +253,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   // V stays in LDS at d >= 128 (its B-operand fragments would not fit in
   // registers next to the dK/dV accumulators); at d = 64 it is in registers.
   constexpr bool V_LDS = D >= 128;
+  constexpr bool FOLD_D = D <= 128;  // -D as the dP accumulator's initial value
 
   __shared__ __attribute__((aligned(1024))) uint16_t q0s[TQ];
   __shared__ __attribute__((aligned(1024))) uint16_t q1s[TQ];
@@ -319,10 +321,15 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 
   TileDma<D, KV_BM, W> qdma;
   qdma.init(q_row, wave, lane);
-  auto coords = [&](int t, int& h, int& q0) {
-    const int hh = t / tiles_per_head;
-    h = g * a.group + hh;
-    q0 = (qt0 + (t - hh * tiles_per_head)) * KV_BM;
+  // Tile coordinates advance incrementally: query rows within a head, then
+  // the next head of the group.
+  const int qfirst = qt0 * KV_BM, qend = nqt * KV_BM;
+  auto advance = [&](int& h, int& q0) {
+    q0 += KV_BM;
+    if (q0 >= qend) {
+      q0 = qfirst;
+      ++h;
+    }
   };
   // Q and dO tiles by DMA.  LSE and D of the tile's rows are loaded raw into
   // a register by threads 0 .. 2 KV_BM - 1 (LSE by the first KV_BM, D by the
@@ -330,9 +337,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   // nothing waits for the load before the tile's products.
   float lsd_raw = 0.f;
   bool lsd_valid = false;
-  auto load = [&](int t, uint16_t* qs, uint16_t* os) {
-    int h, q0;
-    coords(t, h, q0);
+  auto load = [&](int h, int q0, uint16_t* qs, uint16_t* os) {
     if (tid < 2 * KV_BM) {
       const int qr = q0 + (tid & (KV_BM - 1));
       const size_t li = ((size_t)b * a.Hq + h) * a.N + min(qr, a.N - 1);
@@ -345,22 +350,30 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     qdma.load((const uint16_t*)a.dout + rowbase * D, a.N - q0, q_row, os);
   };
   auto store_lsd = [&](float* ls, float* ds) {
-    // LSE in log2 units; rows past the end get +inf, so their probabilities are 0
+    // LSE in log2 units; rows past the end get +inf, so their probabilities
+    // are 0.  D is stored negated where it initialises the dP accumulator.
     if (tid < KV_BM) ls[tid] = lsd_valid ? lsd_raw * 1.4426950408889634f : INFINITY;
-    else if (tid < 2 * KV_BM) ds[tid - KV_BM] = lsd_raw;
+    else if (tid < 2 * KV_BM) ds[tid - KV_BM] = FOLD_D ? -lsd_raw : lsd_raw;
   };
 
   // Causal: the mask is a branch-free select on every tile (cheap next to the
   // 32 products of a tile), so one tile body serves all tiles.
-  auto tile = [&](int t, const uint16_t* qs, const uint16_t* os, const float* ls, const float* dls)
+  auto tile = [&](int q0, const uint16_t* qs, const uint16_t* os, const float* ls, const float* dls)
       __attribute__((always_inline)) {
-    int h, q0;
-    coords(t, h, q0);
-    (void)h;
     // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys;
     // the Q, dO (and V) fragments of k-step kk + 1 are read while k-step kk's
     // two products run
+    // At d <= 128 dP starts from -D (C rows = queries 8 (r / 4) + 4 half +
+    // r % 4, four consecutive rows per 128-bit read), so the products leave
+    // dP - D; at d = 256 (registers too tight) D is subtracted afterwards.
     f32x16_t s = {}, dp = {};
+    if (FOLD_D) {
+      const f32x4_t n0 = *(const f32x4_t*)(dls + 4 * half), n1 = *(const f32x4_t*)(dls + 8 + 4 * half);
+      const f32x4_t n2 = *(const f32x4_t*)(dls + 16 + 4 * half), n3 = *(const f32x4_t*)(dls + 24 + 4 * half);
+      const f32x8_t lo = __builtin_shufflevector(n0, n1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const f32x8_t hi = __builtin_shufflevector(n2, n3, 0, 1, 2, 3, 4, 5, 6, 7);
+      dp = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    }
     {
       frag8_t qa[2], oa[2], va[2];
       auto rd = [&](int kk, int i) __attribute__((always_inline)) {
@@ -379,13 +392,14 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                // MFMA
       }
     }
-    // P = 2^(S c - LSE2), dS = P (dP - D); C rows = queries 8 (r / 4) + 4 half + r % 4
+    // P = 2^(S c - LSE2), dS = P (dP - D)
     const int klim = mykey - q0 - 4 * half;
     u32x4_t pq[2], dsq[2];  // packed P and dS, already the B-operand register tuples
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
       const f32x4_t l4 = *(const f32x4_t*)(ls + 8 * r4 + 4 * half);
-      const f32x4_t d4 = *(const f32x4_t*)(dls + 8 * r4 + 4 * half);
+      f32x4_t d4 = {};
+      if (!FOLD_D) d4 = *(const f32x4_t*)(dls + 8 * r4 + 4 * half);
       float p[4], dsv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -393,7 +407,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         float pv = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
         if (CAUSAL) pv = (8 * r4 + e) < klim ? 0.f : pv;  // query < key
         p[e] = pv;
-        dsv[e] = pv * (dp[r] - d4[e]);
+        dsv[e] = pv * (FOLD_D ? dp[r] : dp[r] - d4[e]);
       }
       pq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, p[0], p[1]);
       pq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, p[2], p[3]);
@@ -428,20 +442,25 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 
   // Tile t lives in buffer t & 1; one barrier per tile, the same number for
   // every wavefront.
+  int lh = g * a.group, lq = qfirst;  // coordinates of the next tile to load
   if (ntiles > 0) {
-    load(0, q0s, o0s);
+    load(lh, lq, q0s, o0s);
     store_lsd(lse0, del0);
   }
+  int cq = lq;  // first query row of the tile being computed
+  advance(lh, lq);
   wait_loads();
   __syncthreads();
   auto step = [&](int t, int buf) __attribute__((always_inline)) {
     if (t + 1 < ntiles) {
-      if (buf) load(t + 1, q0s, o0s);
-      else load(t + 1, q1s, o1s);
+      if (buf) load(lh, lq, q0s, o0s);
+      else load(lh, lq, q1s, o1s);
     }
     fr.pin();
-    if (buf) tile(t, q1s, o1s, lse1, del1);
-    else tile(t, q0s, o0s, lse0, del0);
+    if (buf) tile(cq, q1s, o1s, lse1, del1);
+    else tile(cq, q0s, o0s, lse0, del0);
+    cq = lq;
+    advance(lh, lq);
     if (t + 1 < ntiles) {
       if (buf) store_lsd(lse0, del0);
       else store_lsd(lse1, del1);
