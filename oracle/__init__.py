@@ -18,7 +18,10 @@ Pins (see tests/test_oracle.py): finite differences, PyTorch's CPU fp64
 scaled_dot_product_attention and autograd, closed forms (scale = 0, identical
 keys, causal row 0, N = 1, a hand-worked 2x2 example), invariants (softmax rows
 sum to one, GQA equals MHA with repeated K/V heads, permutation invariance,
-gradient identities) and the tiled model.
+gradient identities) and the tiled model.  The block-sparse variant (an
+optional block mask on the same functions) is pinned by PyTorch's fp64 masked
+scaled_dot_product_attention, finite differences, closed forms and the tiled
+model with block skipping (tests/test_oracle_sparse.py).
 """
 
 from .attention import (  # noqa: F401

@@ -32,6 +32,15 @@ backward, with upstream gradient dO (loss L = sum O * dO):
     dK[j]     = scale * sum_{h in group} sum_i dS[i, j] Q[i]
     dV[j]     = sum_{h in group} sum_i P[i, j] dO[i]
 
+Block-sparse attention (the variant the FlashAttention-1 news page benchmarks
+as "block-sparse FlashAttention", in the paragraph on runtime and memory
+against the A100 baselines; no definition is printed) restricts `allowed`
+further by a block mask over (query block, key block) pairs:
+    allowed   = allowed and mask[i // block, j // block]
+with block = 128 rows by 128 keys on the GPU; every other formula is
+unchanged.  A row whose allowed set is empty gets O = 0, LSE = -inf and
+dQ = 0, and adds nothing to dK or dV.
+
 Readings where the pages are silent (listed again in the design doc):
   * causal orientation: query i may attend key j iff j <= i (the pages only
     say the masked triangle is skipped rather than computed and zeroed;
@@ -62,12 +71,22 @@ def kv_head_of(h: int, hq: int, hkv: int) -> int:
     return h // (hq // hkv)
 
 
-def _allowed(rows: np.ndarray, n_keys: int, causal: bool) -> np.ndarray:
-    """Boolean [len(rows), n_keys] mask: key j visible to query row i."""
+def _allowed(rows: np.ndarray, n_keys: int, causal: bool, head_mask=None, block: int = 128) -> np.ndarray:
+    """Boolean [len(rows), n_keys] mask: key j visible to query row i.
+
+    ``head_mask`` (optional, [ceil(Nq / block), ceil(Nk / block)]) is the
+    block mask of the head: key j is visible only if its (row block, key
+    block) entry is nonzero.
+    """
     cols = np.arange(n_keys)
     if not causal:
-        return np.ones((len(rows), n_keys), dtype=bool)
-    return cols[None, :] <= rows[:, None]
+        ok = np.ones((len(rows), n_keys), dtype=bool)
+    else:
+        ok = cols[None, :] <= rows[:, None]
+    if head_mask is not None:
+        hm = np.asarray(head_mask) != 0
+        ok = ok & hm[rows[:, None] // block, cols[None, :] // block]
+    return ok
 
 
 def _row_softmax(s: np.ndarray, allowed: np.ndarray):
@@ -87,19 +106,21 @@ def _row_softmax(s: np.ndarray, allowed: np.ndarray):
     return p, lse
 
 
-def attention_head_probs(q, k, causal: bool, scale: float) -> np.ndarray:
+def attention_head_probs(q, k, causal: bool, scale: float, head_mask=None, block: int = 128) -> np.ndarray:
     """Full probability matrix P [Nq, Nk] of one head (small inputs only)."""
     q = np.asarray(q, dtype=_F)
     k = np.asarray(k, dtype=_F)
     s = scale * (q @ k.T)
-    p, _ = _row_softmax(s, _allowed(np.arange(q.shape[0]), k.shape[0], causal))
+    p, _ = _row_softmax(s, _allowed(np.arange(q.shape[0]), k.shape[0], causal, head_mask, block))
     return p
 
 
-def attention_head_fwd(q, k, v, causal: bool, scale: float, rows=None, chunk: int = 512):
+def attention_head_fwd(q, k, v, causal: bool, scale: float, rows=None, chunk: int = 512,
+                       head_mask=None, block: int = 128):
     """O and LSE of one head for the query ``rows`` (default: all rows).
 
-    q: [N, d] all query rows of the head; k, v: [N, d] of its K/V head.
+    q: [N, d] all query rows of the head; k, v: [N, d] of its K/V head;
+    head_mask: optional block mask of the head (see ``_allowed``).
     Rows are independent, so they are processed in chunks of whole rows.
     """
     q = np.asarray(q, dtype=_F)
@@ -111,12 +132,13 @@ def attention_head_fwd(q, k, v, causal: bool, scale: float, rows=None, chunk: in
     for c0 in range(0, len(rows), chunk):
         r = rows[c0:c0 + chunk]
         s = scale * (q[r] @ k.T)
-        p, lse[c0:c0 + chunk] = _row_softmax(s, _allowed(r, k.shape[0], causal))
+        p, lse[c0:c0 + chunk] = _row_softmax(s, _allowed(r, k.shape[0], causal, head_mask, block))
         o[c0:c0 + chunk] = p @ v
     return o, lse
 
 
-def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk: int = 512):
+def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk: int = 512,
+                       head_mask=None, block: int = 128):
     """Gradients of L = sum(O * dO) for one query head.
 
     Returns (dq_rows, dk, dv): dq for the query ``rows`` (default: all) and this
@@ -135,7 +157,7 @@ def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk
     for c0 in range(0, len(rows), chunk):
         r = rows[c0:c0 + chunk]
         s = scale * (q[r] @ k.T)
-        p, _ = _row_softmax(s, _allowed(r, k.shape[0], causal))
+        p, _ = _row_softmax(s, _allowed(r, k.shape[0], causal, head_mask, block))
         dp = do[r] @ v.T
         dsum = (p * dp).sum(axis=1)
         ds = p * (dp - dsum[:, None])
@@ -155,22 +177,38 @@ def _check_shapes(q, k, v):
     return b, n, hq, k.shape[2], d
 
 
-def attention_fwd(q, k, v, causal: bool, scale: float):
-    """O [B,N,Hq,d] and LSE [B,Hq,N] in float64."""
+def _head_masks(block_mask, n: int, hkv: int, block: int):
+    """Per-K/V-head block masks: ``block_mask`` is [Hm, nb, nb] with
+    nb = ceil(N / block) and Hm = 1 (shared by every head) or Hkv (query head
+    h uses the mask of its K/V head).  Returns a function g -> mask or None."""
+    if block_mask is None:
+        return lambda g: None
+    m = np.asarray(block_mask)
+    nb = -(-n // block)
+    if m.ndim != 3 or m.shape[1:] != (nb, nb) or m.shape[0] not in (1, hkv):
+        raise ValueError(f"block mask must be [1 or Hkv, {nb}, {nb}], got {m.shape}")
+    return lambda g: m[0] if m.shape[0] == 1 else m[g]
+
+
+def attention_fwd(q, k, v, causal: bool, scale: float, block_mask=None, block: int = 128):
+    """O [B,N,Hq,d] and LSE [B,Hq,N] in float64 (optionally block-sparse)."""
     b, n, hq, hkv, d = _check_shapes(q, k, v)
+    mask_of = _head_masks(block_mask, n, hkv, block)
     o = np.empty((b, n, hq, d), dtype=_F)
     lse = np.empty((b, hq, n), dtype=_F)
     for bi in range(b):
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
             o[bi, :, h], lse[bi, h] = attention_head_fwd(
-                q[bi, :, h], k[bi, :, g], v[bi, :, g], causal, scale)
+                q[bi, :, h], k[bi, :, g], v[bi, :, g], causal, scale,
+                head_mask=mask_of(g), block=block)
     return o, lse
 
 
-def attention_bwd(q, k, v, do, causal: bool, scale: float):
+def attention_bwd(q, k, v, do, causal: bool, scale: float, block_mask=None, block: int = 128):
     """(dQ, dK, dV) in float64; dK/dV sum the contributions of each group."""
     b, n, hq, hkv, d = _check_shapes(q, k, v)
+    mask_of = _head_masks(block_mask, n, hkv, block)
     dq = np.empty((b, n, hq, d), dtype=_F)
     dk = np.zeros((b, n, hkv, d), dtype=_F)
     dv = np.zeros((b, n, hkv, d), dtype=_F)
@@ -178,7 +216,8 @@ def attention_bwd(q, k, v, do, causal: bool, scale: float):
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
             dqh, dkh, dvh = attention_head_bwd(
-                q[bi, :, h], k[bi, :, g], v[bi, :, g], do[bi, :, h], causal, scale)
+                q[bi, :, h], k[bi, :, g], v[bi, :, g], do[bi, :, h], causal, scale,
+                head_mask=mask_of(g), block=block)
             dq[bi, :, h] = dqh
             dk[bi, :, g] += dkh
             dv[bi, :, g] += dvh

@@ -23,6 +23,11 @@ causal mask, key blocks lying wholly above the diagonal are never visited
 (FlashAttention-2 review, "Алгоритм вычисления" subsection), and only blocks
 that straddle the diagonal apply an element mask.
 
+With a block mask (block-sparse attention, which the FlashAttention-1 news
+page benchmarks next to the dense method), key tiles whose (row block, key
+block) entry is zero are skipped the same way; a row that visits no tile gets
+O = 0 and LSE = -inf.
+
 The test compares this model with ``attention.attention_head_fwd`` to 1e-12,
 which pins the pages' equivalence claim in exact (fp64) arithmetic.
 """
@@ -32,12 +37,17 @@ from __future__ import annotations
 import numpy as np
 
 
-def tiled_attention_fwd(q, k, v, causal: bool, scale: float, bm: int = 16, bn: int = 16):
+def tiled_attention_fwd(q, k, v, causal: bool, scale: float, bm: int = 16, bn: int = 16,
+                        head_mask=None, block: int = 128):
     """Online-softmax forward of one head: returns (O [N,d], LSE [N], visited).
 
     ``visited`` counts the (row block, key block) pairs actually computed, so a
-    test can check that fully masked causal blocks were skipped.
+    test can check that fully masked causal blocks were skipped.  ``head_mask``
+    ([ceil(N / block)]^2, optional) is a block mask; ``block`` must then be a
+    multiple of both tile sizes, so that each tile lies in one mask block.
     """
+    if head_mask is not None and (block % bm or block % bn):
+        raise ValueError("the mask block must be a multiple of the tile sizes")
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
@@ -53,6 +63,8 @@ def tiled_attention_fwd(q, k, v, causal: bool, scale: float, bm: int = 16, bn: i
         for j0 in range(0, n_k, bn):
             if causal and j0 > rows[-1]:
                 break  # this key block and every later one is fully masked
+            if head_mask is not None and not head_mask[i0 // block][j0 // block]:
+                continue  # a zero block of the mask: never loaded or computed
             visited += 1
             cols = np.arange(j0, min(j0 + bn, n_k))
             s = scale * (q[rows] @ k[cols].T)
@@ -64,6 +76,9 @@ def tiled_attention_fwd(q, k, v, causal: bool, scale: float, bm: int = 16, bn: i
             l = alpha * l + p.sum(axis=1)
             acc = alpha[:, None] * acc + p @ v[cols]
             m = m_new
+        if not np.isfinite(m).any():  # no tile visited: no allowed key
+            o[rows], lse[rows] = 0.0, -np.inf
+            continue
         o[rows] = acc / l[:, None]
         lse[rows] = m + np.log(l)
     return o, lse, visited

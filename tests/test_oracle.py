@@ -276,7 +276,7 @@ def test_bf16_rounding_is_nearest_even():
 # ---- planted mistakes: each mutated oracle must fail at least one pin ----
 
 def _bwd_mutant(kind):
-    def bwd(q, k, v, do, causal, scale, rows=None, chunk=512):
+    def bwd(q, k, v, do, causal, scale, rows=None, chunk=512, head_mask=None, block=128):
         q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
         r = np.arange(q.shape[0])
         s = scale * (q @ k.T)
@@ -306,7 +306,7 @@ def test_planted_backward_mistakes_are_caught(kind, monkeypatch):
 def test_planted_forward_mistake_is_caught(monkeypatch):
     """A softmax that forgets the causal mask fails the causal-row-0 closed form."""
     real = oa._allowed
-    monkeypatch.setattr(oa, "_allowed", lambda rows, n, causal: real(rows, n, False))
+    monkeypatch.setattr(oa, "_allowed", lambda rows, n, causal, *rest: real(rows, n, False, *rest))
     x = make_inputs(1, 9, 1, 1, 4, "bf16", cfg_id=89)
     o, _ = oa.attention_fwd(x["q"], x["k"], x["v"], True, 0.5)
     assert np.abs(o[0, 0] - x["v"][0, 0]).max() > 1e-6
