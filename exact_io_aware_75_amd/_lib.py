@@ -21,7 +21,9 @@ ATTN_DTYPE_BF16 = 1
 
 # Entry points declared in include/attn.h (checked by the ABI test).
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
-           "attn_bwd_workspace_bytes", "attn_strerror", "attn_last_hip_error", "attn_version")
+           "attn_bwd_workspace_bytes", "attn_fwd_blocksparse", "attn_bwd_blocksparse",
+           "attn_strerror", "attn_last_hip_error", "attn_version")
+SPARSE_BLOCK = 128  # ATTN_SPARSE_BLOCK: rows / keys per block of the block mask
 BWD_STAGES = ("attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq")
 
 
@@ -54,6 +56,11 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
         fn.restype = i
+    lib.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_blocksparse.restype = i
+    lib.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, vp, vp, sz,
+                                         i, i, i, i, i, i, i, f, vp]
+    lib.attn_bwd_blocksparse.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_strerror.argtypes = [i]
@@ -114,8 +121,23 @@ def _dims(q, k):
     return b, n, hq, k.shape[2], d
 
 
-def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
-    """Enqueue the forward pass into preallocated ``o`` and ``lse``."""
+def _check_mask(block_mask, n, hkv, device):
+    """Shape/dtype of a block mask: uint8 [1 or Hkv, nb, nb], nb = ceil(N / 128)."""
+    import torch
+
+    nb = -(-n // SPARSE_BLOCK)
+    if block_mask.dim() != 3 or tuple(block_mask.shape[1:]) != (nb, nb) or block_mask.shape[0] not in (1, hkv):
+        raise ValueError(f"block_mask: shape {tuple(block_mask.shape)}, expected (1 or {hkv}, {nb}, {nb})")
+    _check(block_mask, tuple(block_mask.shape), torch.uint8, device, "block_mask")
+    return int(block_mask.shape[0])
+
+
+def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None, block_mask=None) -> None:
+    """Enqueue the forward pass into preallocated ``o`` and ``lse``.
+
+    ``block_mask`` (optional, uint8 [1 or Hkv, nb, nb] on q's device) selects
+    the block-sparse entry point ``attn_fwd_blocksparse``.
+    """
     import torch
 
     lib = load_library()
@@ -124,10 +146,15 @@ def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None) -> None:
                        (v, (b, n, hkv, d), "v"), (o, (b, n, hq, d), "o")):
         _check(t, shp, q.dtype, q.device, nm)
     _check(lse, (b, hq, n), torch.float32, q.device, "lse")
-    st = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, n, hq, hkv, d,
-                      _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
+    tail = (b, n, hq, hkv, d, _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
+    if block_mask is None:
+        st, name = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), *tail), "attn_fwd"
+    else:
+        mh = _check_mask(block_mask, n, hkv, q.device)
+        st = lib.attn_fwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(block_mask), mh, *tail)
+        name = "attn_fwd_blocksparse"
     if st != 0:
-        raise AttnError(st, "attn_fwd")
+        raise AttnError(st, name)
 
 
 def attn_bwd_workspace_bytes(b: int, n: int, hq: int, hkv: int, d: int) -> int:
@@ -135,18 +162,21 @@ def attn_bwd_workspace_bytes(b: int, n: int, hq: int, hkv: int, d: int) -> int:
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
-             stream=None, stage: str = "attn_bwd") -> None:
+             stream=None, stage: str = "attn_bwd", block_mask=None) -> None:
     """Enqueue the backward pass into preallocated ``dq``, ``dk``, ``dv``.
 
     ``workspace`` is a uint8 device tensor of at least
     ``attn_bwd_workspace_bytes(B, N, Hq, Hkv, d)`` bytes.  ``stage`` selects
     the whole pass ("attn_bwd") or one of its stages (``BWD_STAGES``), which
-    must then be enqueued in order.
+    must then be enqueued in order.  ``block_mask`` (as for ``attn_fwd``)
+    selects ``attn_bwd_blocksparse`` (whole pass only).
     """
     import torch
 
     if stage != "attn_bwd" and stage not in BWD_STAGES:
         raise ValueError(f"unknown backward stage {stage!r}")
+    if block_mask is not None and stage != "attn_bwd":
+        raise ValueError("the block-sparse backward pass has no separate stages")
     lib = load_library()
     b, n, hq, hkv, d = _dims(q, k)
     for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, n, hkv, d), "k"),
@@ -158,9 +188,15 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: 
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = getattr(lib, stage)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
-                             _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, b, n, hq, hkv, d,
-                             _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
+    tail = (_ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, b, n, hq, hkv, d,
+            _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
+    if block_mask is None:
+        st = getattr(lib, stage)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), *tail)
+    else:
+        mh = _check_mask(block_mask, n, hkv, q.device)
+        stage = "attn_bwd_blocksparse"
+        st = lib.attn_bwd_blocksparse(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                      _ptr(block_mask), mh, *tail)
     if st != 0:
         raise AttnError(st, stage)
 
@@ -169,19 +205,22 @@ def _default_scale(d: int, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def forward(q, k, v, causal: bool = False, scale=None, stream=None):
-    """Allocate ``o`` and ``lse`` and run ``attn_fwd``; returns (o, lse)."""
+def forward(q, k, v, causal: bool = False, scale=None, stream=None, block_mask=None):
+    """Allocate ``o`` and ``lse`` and run ``attn_fwd`` (or, with a block
+    mask, ``attn_fwd_blocksparse``); returns (o, lse)."""
     import torch
 
     b, n, hq, _, d = _dims(q, k)
     o = torch.empty_like(q)
     lse = torch.empty((b, hq, n), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, causal, _default_scale(d, scale), stream)
+    attn_fwd(q, k, v, o, lse, causal, _default_scale(d, scale), stream, block_mask=block_mask)
     return o, lse
 
 
-def backward(q, k, v, o, lse, dout, causal: bool = False, scale=None, stream=None, workspace=None):
-    """Allocate gradients (and the workspace if not given) and run ``attn_bwd``."""
+def backward(q, k, v, o, lse, dout, causal: bool = False, scale=None, stream=None, workspace=None,
+             block_mask=None):
+    """Allocate gradients (and the workspace if not given) and run ``attn_bwd``
+    (or, with a block mask, ``attn_bwd_blocksparse``)."""
     import torch
 
     b, n, hq, hkv, d = _dims(q, k)
@@ -189,5 +228,6 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale=None, stream=Non
     if workspace is None:
         workspace = torch.empty(attn_bwd_workspace_bytes(b, n, hq, hkv, d), dtype=torch.uint8,
                                 device=q.device)
-    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, _default_scale(d, scale), stream)
+    attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, _default_scale(d, scale), stream,
+             block_mask=block_mask)
     return dq, dk, dv

@@ -10,6 +10,13 @@ dimension up to 256 and MQA/GQA ("具体实现" section); long sequences up to 6
 
 FLOP accounting: forward 4*B*Hq*N^2*d (two N x N x d products), halved under a
 causal mask; backward 2.5 x forward (five products instead of two).
+Block-sparse: the same count over the computed blocks only (128 x 128 pairs
+each; under a causal mask a diagonal block counts half).
+
+Block-sparse workload (the pages benchmark block-sparse attention next to the
+dense method without giving its pattern): the hidden-2048, d = 128 layer at
+N = 16384, one mask for all heads, every diagonal block plus a seeded 25% of
+the other blocks.
 """
 
 from __future__ import annotations
@@ -67,6 +74,35 @@ def gqa(hkv: int) -> Shape:
 def wide_head() -> Shape:
     """B=4, N=4096, H=8, d=256, causal (MHA)."""
     return Shape("mha_d256", 5, 4, 4096, 8, 8, 256, "bf16", True)
+
+
+BLOCKSPARSE_DENSITY = 0.25
+
+
+def blocksparse(causal: bool, n: int = 16384) -> Shape:
+    """Hidden size 2048, d = 128 (H = 16), B = 16384 / N, block mask of
+    BLOCKSPARSE_DENSITY plus the diagonal."""
+    return Shape("blocksparse_h2048_d128", 6, TOKENS // n, n, 16, 16, 128, "bf16", causal)
+
+
+def masked_fwd_flops(s: Shape, mask, block: int = 128) -> float:
+    """Forward FLOPs over the computed blocks of ``mask`` ([1 or Hkv, nb, nb]):
+    4 * d * block^2 per (head, batch, computed block), a causal diagonal block
+    counting half and blocks past the diagonal not at all.  N must be a
+    multiple of ``block``."""
+    import numpy as np
+
+    if s.n % block:
+        raise ValueError("N must be a multiple of the block size")
+    m = np.asarray(mask) != 0
+    nb = m.shape[1]
+    if s.causal:
+        w = np.tril(np.ones((nb, nb))) - 0.5 * np.eye(nb)
+    else:
+        w = np.ones((nb, nb))
+    per_mask = (m * w).sum(axis=(1, 2))  # weighted block count per mask
+    heads_per_mask = s.hq if m.shape[0] == 1 else s.hq // s.hkv
+    return 4.0 * s.d * block * block * s.b * heads_per_mask * float(per_mask.sum())
 
 
 def all_shapes():

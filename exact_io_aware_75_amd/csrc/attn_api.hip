@@ -55,6 +55,22 @@ int check_device() {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Block-mask arguments of the block-sparse entry points.
+int check_mask(const unsigned char* block_mask, int mask_heads, int N, int Hkv, attn::SparseArgs* sp) {
+  if (!block_mask) return ATTN_ERR_NULLPTR;
+  if (mask_heads != 1 && mask_heads != Hkv) return ATTN_ERR_SHAPE;
+  if (N > ATTN_SPARSE_MAX_N) return ATTN_ERR_TOO_LARGE;
+  static_assert(ATTN_SPARSE_BLOCK == attn::SPARSE_BLOCK &&
+                    ATTN_SPARSE_MAX_N == attn::SPARSE_BLOCK * attn::SPARSE_MAX_NB,
+                "header constants match the kernels");
+  sp->bmask = reinterpret_cast<const uint8_t*>(block_mask);
+  sp->nb = (N + ATTN_SPARSE_BLOCK - 1) / ATTN_SPARSE_BLOCK;
+  sp->mask_hstride = mask_heads == 1 ? 0 : sp->nb * sp->nb;
+  return ATTN_OK;
+}
+
+const attn::SparseArgs kDense = {nullptr, 0, 0};
+
 }  // namespace
 
 namespace attn {
@@ -70,10 +86,11 @@ BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int /*Hkv*/, int d) {
 
 }  // namespace attn
 
-extern "C" {
+namespace {
 
-int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int N,
-             int Hq, int Hkv, int d, int dtype, int causal, float scale, void* stream) {
+int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
+               const unsigned char* block_mask, int mask_heads, int B, int N, int Hq, int Hkv,
+               int d, int dtype, int causal, float scale, void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULLPTR;
   int st = check_shape(B, N, Hq, Hkv, d);
   if (st != ATTN_OK) return st;
@@ -81,6 +98,11 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
     return ATTN_ERR_ALIGN;
   if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  attn::SparseArgs sp = kDense;
+  if (block_mask || mask_heads) {
+    st = check_mask(block_mask, mask_heads, N, Hkv, &sp);
+    if (st != ATTN_OK) return st;
+  }
   st = check_device();
   if (st != ATTN_OK) return st;
 
@@ -97,6 +119,7 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
   a.group = Hq / Hkv;
   a.neg_scale = scale < 0.f ? 1 : 0;
   a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
+  a.sp = sp;
   hipError_t e = attn::launch_fwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -104,6 +127,23 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, i
     return ATTN_ERR_HIP;
   }
   return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int N,
+             int Hq, int Hkv, int d, int dtype, int causal, float scale, void* stream) {
+  return fwd_common(q, k, v, o, lse, nullptr, 0, B, N, Hq, Hkv, d, dtype, causal, scale, stream);
+}
+
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const unsigned char* block_mask, int mask_heads, int B, int N, int Hq,
+                         int Hkv, int d, int dtype, int causal, float scale, void* stream) {
+  if (!block_mask) return ATTN_ERR_NULLPTR;
+  return fwd_common(q, k, v, o, lse, block_mask, mask_heads, B, N, Hq, Hkv, d, dtype, causal,
+                    scale, stream);
 }
 
 size_t attn_bwd_workspace_bytes(int B, int N, int Hq, int Hkv, int d) {
@@ -115,10 +155,10 @@ size_t attn_bwd_workspace_bytes(int B, int N, int Hq, int Hkv, int d) {
 
 namespace {
 
-int bwd_common(int stages, const void* q, const void* k, const void* v, const void* o,
-               const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
-               size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
-               int causal, float scale, void* stream) {
+int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, const void* q,
+               const void* k, const void* v, const void* o, const void* dout, const float* lse,
+               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+               int N, int Hq, int Hkv, int d, int dtype, int causal, float scale, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULLPTR;
   int st = check_shape(B, N, Hq, Hkv, d);
   if (st != ATTN_OK) return st;
@@ -130,6 +170,11 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   const attn::BwdWorkspace ws = attn::bwd_workspace_layout(B, N, Hq, Hkv, d);
   if (!workspace || workspace_bytes < ws.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  attn::SparseArgs sp = kDense;
+  if (block_mask || mask_heads) {
+    st = check_mask(block_mask, mask_heads, N, Hkv, &sp);
+    if (st != ATTN_OK) return st;
+  }
   st = check_device();
   if (st != ATTN_OK) return st;
 
@@ -151,6 +196,7 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
   a.group = Hq / Hkv;
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.sp = sp;
   hipError_t e = attn::launch_bwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0, stages,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -173,10 +219,19 @@ extern "C" {
   q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, N, Hq, Hkv, d, dtype,   \
       causal, scale, stream
 
-int attn_bwd(ATTN_BWD_ARGS) { return bwd_common(7, ATTN_BWD_PASS); }
-int attn_bwd_preprocess(ATTN_BWD_ARGS) { return bwd_common(1, ATTN_BWD_PASS); }
-int attn_bwd_dkdv(ATTN_BWD_ARGS) { return bwd_common(2, ATTN_BWD_PASS); }
-int attn_bwd_dq(ATTN_BWD_ARGS) { return bwd_common(4, ATTN_BWD_PASS); }
+int attn_bwd(ATTN_BWD_ARGS) { return bwd_common(7, nullptr, 0, ATTN_BWD_PASS); }
+int attn_bwd_preprocess(ATTN_BWD_ARGS) { return bwd_common(1, nullptr, 0, ATTN_BWD_PASS); }
+int attn_bwd_dkdv(ATTN_BWD_ARGS) { return bwd_common(2, nullptr, 0, ATTN_BWD_PASS); }
+int attn_bwd_dq(ATTN_BWD_ARGS) { return bwd_common(4, nullptr, 0, ATTN_BWD_PASS); }
+
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, const unsigned char* block_mask,
+                         int mask_heads, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
+                         int causal, float scale, void* stream) {
+  if (!block_mask) return ATTN_ERR_NULLPTR;
+  return bwd_common(7, block_mask, mask_heads, ATTN_BWD_PASS);
+}
 
 #undef ATTN_BWD_ARGS
 #undef ATTN_BWD_PASS

@@ -228,8 +228,12 @@ template <int D> struct BwdOcc { static constexpr int WAVES_PER_SIMD = D <= 128 
 // Causal dQ keeps four (the wavefronts of a diagonal block have unequal trip
 // counts), and so does dK/dV, where eight measured 3% slower non-causal and
 // 14% slower causal (a 256-key block computes more masked diagonal tiles).
+// Block-sparse dQ keeps four too, so that a workgroup's 128 queries are one
+// row of the block mask (as a dK/dV workgroup's 128 keys are one column).
 template <int D, bool CAUSAL> struct DkdvWG { static constexpr int WAVES = 4; };
-template <int D, bool CAUSAL> struct DqWG { static constexpr int WAVES = (D <= 128 && !CAUSAL) ? 8 : 4; };
+template <int D, bool CAUSAL, bool SPARSE = false> struct DqWG {
+  static constexpr int WAVES = (D <= 128 && !CAUSAL && !SPARSE) ? 8 : 4;
+};
 template <int D, int W> struct BwdBounds {
   static constexpr int THREADS = 64 * W;
   static constexpr int MIN_WG = BwdOcc<D>::WAVES_PER_SIMD * 4 / W;
@@ -241,7 +245,7 @@ template <int D, int W> struct BwdBounds {
 constexpr int KV_BM = 32;   // query rows per tile
 constexpr int BWD_PFT = 2;  // transposed fragments read ahead in dV/dK
 
-template <typename Tag, int D, bool CAUSAL>
+template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 __global__ void __launch_bounds__((BwdBounds<D, DkdvWG<D, CAUSAL>::WAVES>::THREADS),
                                   (BwdBounds<D, DkdvWG<D, CAUSAL>::WAVES>::MIN_WG))
 attn_bwd_dkdv_kernel(BwdArgs a) {
@@ -254,6 +258,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   // registers next to the dK/dV accumulators); at d = 64 it is in registers.
   constexpr bool V_LDS = D >= 128;
   constexpr bool FOLD_D = D <= 128;  // -D as the dP accumulator's initial value
+  static_assert(!SPARSE || KV_BN == SPARSE_BLOCK, "one workgroup per column of the block mask");
 
   __shared__ __attribute__((aligned(1024))) uint16_t q0s[TQ];
   __shared__ __attribute__((aligned(1024))) uint16_t q1s[TQ];
@@ -261,6 +266,9 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t o1s[TQ];
   __shared__ __attribute__((aligned(1024))) uint16_t vblk[V_LDS ? KV_BN * D : 8];
   __shared__ __attribute__((aligned(16))) float lse0[KV_BM], lse1[KV_BM], del0[KV_BM], del1[KV_BM];
+  // block-sparse: the query blocks this key block meets, in increasing order
+  __shared__ uint16_t blist[SPARSE ? SPARSE_MAX_NB : 1];
+  __shared__ int bcount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -315,7 +323,24 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   // (causal: only tiles with a row >= k0)
   const int nqt = (a.N + KV_BM - 1) / KV_BM;
   const int qt0 = CAUSAL ? k0 / KV_BM : 0;
-  const int tiles_per_head = nqt - qt0;
+  int tiles_per_head = nqt - qt0;
+  // Block-sparse: the query tiles of the listed query blocks (causal: from
+  // the diagonal block on), KV_BM rows at a time; only the last block of the
+  // sequence can be ragged, and it can only be the last listed.
+  int nlist = 0;
+  if constexpr (SPARSE) {
+    if (wave == 0) {
+      const uint8_t* mcol = a.sp.bmask + (size_t)g * a.sp.mask_hstride + kb;
+      const int cnt = compact_mask(mcol, a.sp.nb, CAUSAL ? kb : 0, a.sp.nb, blist, lane);
+      if (lane == 0) bcount = cnt;
+    }
+    __syncthreads();
+    nlist = __builtin_amdgcn_readfirstlane(bcount);
+    constexpr int QPB = SPARSE_BLOCK / KV_BM;  // query tiles per block
+    tiles_per_head = nlist * QPB;
+    if (nlist > 0 && lds_uniform(blist, nlist - 1) == a.sp.nb - 1)
+      tiles_per_head -= QPB - (a.N - (a.sp.nb - 1) * SPARSE_BLOCK + KV_BM - 1) / KV_BM;
+  }
   const int ntiles = tiles_per_head * a.group;
   const float c = a.scale_log2;  // scale * log2(e), signed
 
@@ -324,9 +349,19 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   // Tile coordinates advance incrementally: query rows within a head, then
   // the next head of the group.
   const int qfirst = qt0 * KV_BM, qend = nqt * KV_BM;
+  int li = 0;  // block-sparse: list entry of the next tile to load
   auto advance = [&](int& h, int& q0) {
     q0 += KV_BM;
-    if (q0 >= qend) {
+    if constexpr (SPARSE) {
+      const int blk = q0 - KV_BM - (q0 - KV_BM) % SPARSE_BLOCK;  // first row of the tile's block
+      if (q0 >= min(blk + SPARSE_BLOCK, a.N)) {
+        if (++li == nlist) {
+          li = 0;
+          ++h;
+        }
+        q0 = lds_uniform(blist, li) * SPARSE_BLOCK;
+      }
+    } else if (q0 >= qend) {
       q0 = qfirst;
       ++h;
     }
@@ -443,12 +478,13 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   // Tile t lives in buffer t & 1; one barrier per tile, the same number for
   // every wavefront.
   int lh = g * a.group, lq = qfirst;  // coordinates of the next tile to load
+  if constexpr (SPARSE) lq = nlist > 0 ? lds_uniform(blist, 0) * SPARSE_BLOCK : 0;
   if (ntiles > 0) {
     load(lh, lq, q0s, o0s);
     store_lsd(lse0, del0);
   }
   int cq = lq;  // first query row of the tile being computed
-  advance(lh, lq);
+  if (!SPARSE || ntiles > 0) advance(lh, lq);  // (an empty list has no entry to advance to)
   wait_loads();
   __syncthreads();
   auto step = [&](int t, int buf) __attribute__((always_inline)) {
@@ -503,11 +539,11 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 // 32-key tiles run the d = 128 dQ pass 18% faster.)
 template <int D> struct DqTile { static constexpr int BN = D == 64 ? 128 : 32; };
 
-template <typename Tag, int D, bool CAUSAL>
-__global__ void __launch_bounds__((BwdBounds<D, DqWG<D, CAUSAL>::WAVES>::THREADS),
-                                  (BwdBounds<D, DqWG<D, CAUSAL>::WAVES>::MIN_WG))
+template <typename Tag, int D, bool CAUSAL, bool SPARSE>
+__global__ void __launch_bounds__((BwdBounds<D, DqWG<D, CAUSAL, SPARSE>::WAVES>::THREADS),
+                                  (BwdBounds<D, DqWG<D, CAUSAL, SPARSE>::WAVES>::MIN_WG))
 attn_bwd_dq_kernel(BwdArgs a) {
-  constexpr int W = DqWG<D, CAUSAL>::WAVES;
+  constexpr int W = DqWG<D, CAUSAL, SPARSE>::WAVES;
   constexpr int DQ_BM = 32 * W;  // queries per workgroup
   constexpr int BN = DqTile<D>::BN;  // keys per tile
   constexpr int TILE = BN * D;
@@ -515,11 +551,16 @@ attn_bwd_dq_kernel(BwdArgs a) {
   constexpr int NSB = BN / 32;   // 32-key sub-blocks per tile
   constexpr int NDB = D / 32;
   constexpr int NKS = BN / 16;   // k-steps over keys in dQ^T += K^T dS^T
+  constexpr int TPB = SPARSE_BLOCK / BN;  // key tiles per block of the mask
+  static_assert(!SPARSE || DQ_BM == SPARSE_BLOCK, "one workgroup per row of the block mask");
 
   __shared__ __attribute__((aligned(1024))) uint16_t k0s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
+  // block-sparse: the key blocks this row block computes, in increasing order
+  __shared__ uint16_t blist[SPARSE ? SPARSE_MAX_NB : 1];
+  __shared__ int bcount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -543,6 +584,32 @@ attn_bwd_dq_kernel(BwdArgs a) {
   const int wrow0 = row0 + wave * 32;
   const int qrow = wrow0 + l32;
   const int qsafe = min(qrow, a.N - 1);
+
+  // ---- block-sparse: list the allowed key blocks of row block rb ----
+  int nlist = 0;
+  if constexpr (SPARSE) {
+    if (wave == 0) {
+      const uint8_t* mrow = a.sp.bmask + (size_t)g * a.sp.mask_hstride + (size_t)rb * a.sp.nb;
+      const int cnt = compact_mask(mrow, 1, 0, CAUSAL ? rb + 1 : a.sp.nb, blist, lane);
+      if (lane == 0) bcount = cnt;
+    }
+    __syncthreads();
+    nlist = __builtin_amdgcn_readfirstlane(bcount);
+    if (nlist == 0) {  // no allowed key in any row of the block: dQ = 0
+      if (qrow < a.N) {
+        uint16_t* dqr = (uint16_t*)a.dq + (((size_t)b * a.N + qrow) * a.Hq + h) * D;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) *(u32x4_t*)(dqr + 16 * i + 8 * half) = (u32x4_t){0u, 0u, 0u, 0u};
+      }
+      return;
+    }
+  }
+  // key tile of loop step j: j itself, or (block-sparse) tile j % TPB of the
+  // (j / TPB)-th listed block
+  auto ktile = [&](int j) __attribute__((always_inline)) {
+    if constexpr (SPARSE) return lds_uniform(blist, j / TPB) * TPB + j % TPB;
+    else return j;
+  };
 
   // Q and dO as B operands (lane = query, 8 consecutive d per k-step)
   frag8_t qf[NKK], of[NKK];
@@ -575,15 +642,25 @@ attn_bwd_dq_kernel(BwdArgs a) {
     nwave = min(ntiles_all, (wrow0 + 31) / BN + 1);
     nfull = min(nfull, (wrow0 + 1) / BN);
   }
+  if constexpr (SPARSE) {
+    // bounds on the key tile index -> counts of loop steps (every listed
+    // block but the last lies wholly below each bound)
+    const int last = lds_uniform(blist, nlist - 1);
+    auto steps_below = [&](int bound) { return (nlist - 1) * TPB + min(max(bound - last * TPB, 0), TPB); };
+    ntiles = steps_below(ntiles);
+    nwave = steps_below(nwave);
+    nfull = steps_below(nfull);
+  }
 
   f32x16_t dq_acc[NDB];  // dQ^T: lane = query, rows = d
 #pragma unroll
   for (int i = 0; i < NDB; ++i) dq_acc[i] = (f32x16_t){};
 
   auto load = [&](int j, uint16_t* ks, uint16_t* vs) {
-    const size_t off = (size_t)j * BN * kv_row;
-    dma.load(kbase + off, a.N - j * BN, kv_row, ks);
-    dma.load(vbase + off, a.N - j * BN, kv_row, vs);
+    const int kt = ktile(j);
+    const size_t off = (size_t)kt * BN * kv_row;
+    dma.load(kbase + off, a.N - kt * BN, kv_row, ks);
+    dma.load(vbase + off, a.N - kt * BN, kv_row, vs);
   };
 
   auto tile = [&](int j, const uint16_t* ks, const uint16_t* vs, auto mask_tag)
@@ -592,7 +669,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
     // Per 32-key sub-block: S^T = K Q^T and dP^T = V dO^T for this
     // wavefront's 32 queries, then dS^T = P^T (dP^T - D) with
     // P^T = 2^(S^T c - LSE2); rows = keys 32 sb + 8 (r / 4) + 4 half + r % 4.
-    const int key0 = j * BN;
+    const int key0 = MASK ? ktile(j) * BN : 0;
     int lim = 0;
     if (MASK) {
       lim = a.N - 1 - key0 - 4 * half;
@@ -701,8 +778,11 @@ attn_bwd_dq_kernel(BwdArgs a) {
 
 }  // namespace
 
-template <typename Tag, int D, bool CAUSAL>
+template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
+  if (SPARSE && (a.sp.bmask == nullptr || a.sp.nb != (a.N + SPARSE_BLOCK - 1) / SPARSE_BLOCK ||
+                 a.sp.nb > SPARSE_MAX_NB))
+    return hipErrorInvalidValue;
   const long long rows = (long long)a.B * a.N * a.Hq;
   if (stages & 1) {
     constexpr int ROWS = 256 / (D / 8);
@@ -716,16 +796,16 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     constexpr int W = DkdvWG<D, CAUSAL>::WAVES;
     const long long grid = (long long)((a.N + 32 * W - 1) / (32 * W)) * a.Hkv * a.B;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL>), dim3((unsigned)grid), dim3(64 * W), 0,
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (stages & 4) {
-    constexpr int W = DqWG<D, CAUSAL>::WAVES;
+    constexpr int W = DqWG<D, CAUSAL, SPARSE>::WAVES;
     const long long grid = (long long)((a.N + 32 * W - 1) / (32 * W)) * a.Hq * a.B;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL>), dim3((unsigned)grid), dim3(64 * W), 0,
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W), 0,
                        stream, a);
     return hipGetLastError();
   }
@@ -734,9 +814,14 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
 
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, int d, bool causal, int stages,
                       hipStream_t stream) {
-#define ATTN_BWD_CASE(TAG, DD)                                                     \
-  if (d == DD) return causal ? launch_bwd_t<TAG, DD, true>(a, stages, stream)     \
-                             : launch_bwd_t<TAG, DD, false>(a, stages, stream);
+#define ATTN_BWD_CASE(TAG, DD)                                                            \
+  if (d == DD) {                                                                          \
+    if (a.sp.bmask)                                                                       \
+      return causal ? launch_bwd_t<TAG, DD, true, true>(a, stages, stream)                \
+                    : launch_bwd_t<TAG, DD, false, true>(a, stages, stream);              \
+    return causal ? launch_bwd_t<TAG, DD, true, false>(a, stages, stream)                 \
+                  : launch_bwd_t<TAG, DD, false, false>(a, stages, stream);               \
+  }
   if (bf16) {
     ATTN_BWD_CASE(Bf16Tag, 64)
     ATTN_BWD_CASE(Bf16Tag, 128)

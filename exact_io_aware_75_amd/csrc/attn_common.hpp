@@ -87,6 +87,32 @@ __device__ __forceinline__ float wave_xor32(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// Block-sparse attention: compacts the indices i in [first, last) whose mask
+// entry p[i * stride] is nonzero, in increasing order, into list[] (LDS), and
+// returns their count (wave-uniform).  Run by one whole wavefront; the
+// workgroup synchronises before other wavefronts read the list.
+__device__ __forceinline__ int compact_mask(const uint8_t* p, int stride, int first, int last,
+                                            uint16_t* list, int lane) {
+  int cnt = 0;
+  for (int base = first; base < last; base += 64) {
+    const int i = base + lane;
+    const bool on = i < last && p[(size_t)i * stride] != 0;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+    if (on) {
+      const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      list[cnt + pos] = (uint16_t)i;
+    }
+    cnt += __builtin_popcountll(bal);
+  }
+  return cnt;
+}
+
+// Wave-uniform read of an LDS list entry (kept in a scalar register).
+__device__ __forceinline__ int lds_uniform(const uint16_t* list, int i) {
+  return __builtin_amdgcn_readfirstlane((int)list[i]);
+}
+
 // Block index remap so that consecutive logical work items run on the same
 // XCD (the hardware dispatches workgroup i to XCD i % 8).  `total` must be a
 // multiple of 8 for the remap to be a bijection; otherwise identity.

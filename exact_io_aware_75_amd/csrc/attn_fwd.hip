@@ -62,9 +62,10 @@ namespace {
 // eight, one workgroup per CU at two wavefronts per SIMD, so each K/V tile is
 // staged once per 256 query rows.  Causal: four, since the wavefronts of a
 // diagonal block have unequal trip counts and wait for the longest at every
-// barrier.  d = 256: four (one wavefront per SIMD).
-template <int D, bool CAUSAL> struct FwdWG {
-  static constexpr int WAVES = (D <= 128 && !CAUSAL) ? 8 : 4;
+// barrier.  d = 256: four (one wavefront per SIMD).  Block-sparse: four, so
+// that a workgroup's 128 rows are one row of the block mask.
+template <int D, bool CAUSAL, bool SPARSE = false> struct FwdWG {
+  static constexpr int WAVES = (D <= 128 && !CAUSAL && !SPARSE) ? 8 : 4;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BM = WAVES * 32;
 };
@@ -91,9 +92,9 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Wavefronts per SIMD the register budget is cut for: two for d <= 128; at
 // d = 256 the resident Q (64 registers) and O^T (128) leave too little for two.
-template <int D, bool CAUSAL> struct FwdOcc {
+template <int D, bool CAUSAL, bool SPARSE> struct FwdOcc {
   static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1;
-  static constexpr int MIN_WG_PER_CU = WAVES_PER_SIMD * 4 / FwdWG<D, CAUSAL>::WAVES;  // launch-bounds form
+  static constexpr int MIN_WG_PER_CU = WAVES_PER_SIMD * 4 / FwdWG<D, CAUSAL, SPARSE>::WAVES;  // launch-bounds form
 };
 
 template <int I, int N, typename F>
@@ -112,20 +113,22 @@ template <int D> struct FwdPrefetch {
   static constexpr int V = 2;
 };
 
-template <typename Tag, int D, bool CAUSAL>
-__global__ void __launch_bounds__((FwdWG<D, CAUSAL>::THREADS), (FwdOcc<D, CAUSAL>::MIN_WG_PER_CU))
+template <typename Tag, int D, bool CAUSAL, bool SPARSE>
+__global__ void __launch_bounds__((FwdWG<D, CAUSAL, SPARSE>::THREADS), (FwdOcc<D, CAUSAL, SPARSE>::MIN_WG_PER_CU))
 attn_fwd_kernel(FwdArgs a) {
   constexpr int BN = FwdTile<D>::BN;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILE = BN * D;          // elements per K or V tile (8192)
-  constexpr int FWD_WAVES = FwdWG<D, CAUSAL>::WAVES;
-  constexpr int FWD_BM = FwdWG<D, CAUSAL>::BM;
-  constexpr int LPT = TILE / 8 / FwdWG<D, CAUSAL>::THREADS;  // 16-byte loads per thread per tensor
+  constexpr int FWD_WAVES = FwdWG<D, CAUSAL, SPARSE>::WAVES;
+  constexpr int FWD_BM = FwdWG<D, CAUSAL, SPARSE>::BM;
+  constexpr int LPT = TILE / 8 / FwdWG<D, CAUSAL, SPARSE>::THREADS;  // 16-byte loads per thread per tensor
   constexpr int NKK = D / 16;           // MFMA k-steps over d
   constexpr int NSB = BN / 32;          // 32-key sub-blocks per tile
   constexpr int NDB = D / 32;           // 32-wide d blocks of O
   constexpr int NKS = BN / 16;          // k-steps over keys in P V
-  static_assert(TILE == 8192 && LPT * 8 * FwdWG<D, CAUSAL>::THREADS == TILE, "tile shape");
+  static_assert(TILE == 8192 && LPT * 8 * FwdWG<D, CAUSAL, SPARSE>::THREADS == TILE, "tile shape");
+  constexpr int TPB = SPARSE_BLOCK / BN;  // key tiles per block of the mask
+  static_assert(!SPARSE || FWD_BM == SPARSE_BLOCK, "one workgroup per row of the block mask");
 
   // K and V tiles are double-buffered separately: iteration j reads K_{j+1}
   // and V_j while K_{j+2} and V_{j+1} stream in.  Four separate objects, so
@@ -134,6 +137,9 @@ attn_fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(1024))) uint16_t k1s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v0s[TILE];
   __shared__ __attribute__((aligned(1024))) uint16_t v1s[TILE];
+  // block-sparse: the key blocks this row block computes, in increasing order
+  __shared__ uint16_t blist[SPARSE ? SPARSE_MAX_NB : 1];
+  __shared__ int bcount;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -162,6 +168,34 @@ attn_fwd_kernel(FwdArgs a) {
   const int qrow = wrow0 + l32;                 // this lane's query row
   const bool qvalid = qrow < a.N;
 
+  // ---- block-sparse: list the allowed key blocks of row block rb ----
+  // (causal: blocks past the diagonal are dropped whatever the mask says)
+  int nlist = 0;
+  if constexpr (SPARSE) {
+    if (wave == 0) {
+      const uint8_t* mrow = a.sp.bmask + (size_t)g * a.sp.mask_hstride + (size_t)rb * a.sp.nb;
+      const int cnt = compact_mask(mrow, 1, 0, CAUSAL ? rb + 1 : a.sp.nb, blist, lane);
+      if (lane == 0) bcount = cnt;
+    }
+    __syncthreads();
+    nlist = __builtin_amdgcn_readfirstlane(bcount);
+    if (nlist == 0) {  // no allowed key in any row of the block: O = 0, LSE = -inf
+      if (qvalid) {
+        uint16_t* orow = (uint16_t*)a.o + ((size_t)b * a.N * a.Hq + h) * D + (size_t)qrow * q_row;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) *(u32x4_t*)(orow + 16 * i + 8 * half) = (u32x4_t){0u, 0u, 0u, 0u};
+        if (half == 0) a.lse[((size_t)b * a.Hq + h) * a.N + qrow] = -INFINITY;
+      }
+      return;
+    }
+  }
+  // key tile computed in loop step j: j itself, or (block-sparse) tile
+  // j % TPB of the (j / TPB)-th listed block
+  auto ktile = [&](int j) __attribute__((always_inline)) {
+    if constexpr (SPARSE) return lds_uniform(blist, j / TPB) * TPB + j % TPB;
+    else return j;
+  };
+
   // ---- Q fragments (B operand of S^T = K Q^T), resident for the whole loop ----
   frag8_t qf[NKK];
   {
@@ -185,6 +219,16 @@ attn_fwd_kernel(FwdArgs a) {
     ntiles = min(ntiles_all, (min(row0 + FWD_BM, a.N) - 1) / BN + 1);
     nwave = min(ntiles_all, (wrow0 + 31) / BN + 1);
     nfull = min(nfull, (wrow0 + 1) / BN);
+  }
+  if constexpr (SPARSE) {
+    // The counts above are bounds on the key tile index.  Every listed block
+    // but the last lies wholly below each of them (only the last can be the
+    // diagonal or the ragged end), so each becomes a count of loop steps.
+    const int last = lds_uniform(blist, nlist - 1);
+    auto steps_below = [&](int bound) { return (nlist - 1) * TPB + min(max(bound - last * TPB, 0), TPB); };
+    ntiles = steps_below(ntiles);
+    nwave = steps_below(nwave);
+    nfull = steps_below(nfull);
   }
 
   // ---- HBM -> LDS tile loads: thread (wave, lane) fills chunk (4 i + wave) * 64 + lane ----
@@ -218,8 +262,8 @@ attn_fwd_kernel(FwdArgs a) {
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lptr_t)(dstt + dst), 16, off[i], 0, 0, 0);
     }
   };
-  auto load_k = [&](int j, uint16_t* dstt) { load_one(j, kbase, ld_koff, dstt); };
-  auto load_v = [&](int j, uint16_t* dstt) { load_one(j, vbase, ld_voff, dstt); };
+  auto load_k = [&](int j, uint16_t* dstt) { load_one(ktile(j), kbase, ld_koff, dstt); };
+  auto load_v = [&](int j, uint16_t* dstt) { load_one(ktile(j), vbase, ld_voff, dstt); };
 
   // ---- per-lane LDS read offsets (elements, within one tile) ----
   // K (A operand of S^T): row 32 sb + l32, logical chunk 2 kk + half.
@@ -330,7 +374,7 @@ attn_fwd_kernel(FwdArgs a) {
     }
   };
   auto apply_mask = [&](f32x16_t* s, int j) __attribute__((always_inline)) {
-    const int key0 = j * BN;
+    const int key0 = ktile(j) * BN;
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
@@ -495,14 +539,21 @@ attn_fwd_kernel(FwdArgs a) {
 
 }  // namespace
 
-template <typename Tag, int D, bool CAUSAL>
-hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  const int nblk = (a.N + FwdWG<D, CAUSAL>::BM - 1) / FwdWG<D, CAUSAL>::BM;
+template <typename Tag, int D, bool CAUSAL, bool SPARSE>
+hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t stream) {
+  using WG = FwdWG<D, CAUSAL, SPARSE>;
+  const int nblk = (a.N + WG::BM - 1) / WG::BM;
   const long long total = (long long)nblk * a.Hq * a.B;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL>), dim3((unsigned)total), dim3(FwdWG<D, CAUSAL>::THREADS),
-                     0, stream, a);
+  if (SPARSE && (a.sp.bmask == nullptr || a.sp.nb != nblk || a.sp.nb > SPARSE_MAX_NB)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)total), dim3(WG::THREADS), 0,
+                     stream, a);
   return hipGetLastError();
+}
+
+template <typename Tag, int D, bool CAUSAL>
+hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  return a.sp.bmask ? launch_fwd_s<Tag, D, CAUSAL, true>(a, stream) : launch_fwd_s<Tag, D, CAUSAL, false>(a, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream) {

@@ -4,8 +4,22 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace attn {
+
+// Block-sparse attention: the mask has one entry per (query block, key block)
+// pair of SPARSE_BLOCK x SPARSE_BLOCK; the kernels keep the allowed blocks of
+// one row (or column) of the mask as a list in LDS, so nb <= SPARSE_MAX_NB.
+constexpr int SPARSE_BLOCK = 128;
+constexpr int SPARSE_MAX_NB = 2048;
+
+// Optional block mask shared by the forward and backward argument structs.
+struct SparseArgs {
+  const uint8_t* bmask;  // null: dense; else uint8 [mask heads][nb][nb], nonzero = computed
+  int nb;                // ceil(N / SPARSE_BLOCK)
+  int mask_hstride;      // entries between the masks of consecutive K/V heads (0: one mask)
+};
 
 struct FwdArgs {
   const void* q;  // [B, N, Hq, d]
@@ -17,6 +31,7 @@ struct FwdArgs {
   int group;         // Hq / Hkv
   int neg_scale;     // 1 if scale < 0 (folded into Q's sign)
   float scale_log2;  // |scale| * log2(e)
+  SparseArgs sp;
 };
 
 struct BwdArgs {
@@ -34,6 +49,7 @@ struct BwdArgs {
   int group;
   float scale;       // signed softmax scale
   float scale_log2;  // scale * log2(e)
+  SparseArgs sp;
 };
 
 // Workspace layout of the backward pass (offsets in bytes, 256-byte aligned).

@@ -7,14 +7,17 @@ oracle see bit-identical values (the oracle upcasts them exactly to float64).
 Recipe: every tensor is drawn in float32 from
 ``numpy.random.default_rng(SeedSequence([cfg_id, N, tensor_id, seed]))`` with
 tensor ids Q=0, K=1, V=2, dO=3, then rounded to nearest-even to bf16 or fp16.
-Causal and non-causal runs reuse the same tensors.
+Causal and non-causal runs reuse the same tensors.  Block masks for
+block-sparse attention are drawn the same way (tensor id 4): each (query
+block, key block) entry is 1 with a given probability, optionally with every
+diagonal block set.
 """
 
 from __future__ import annotations
 
 import numpy as np
 
-TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3}
+TENSOR_ID = {"q": 0, "k": 1, "v": 2, "do": 3, "mask": 4}
 
 
 def round_to_bf16(x: np.ndarray) -> np.ndarray:
@@ -57,6 +60,19 @@ def make_inputs(b: int, n: int, hq: int, hkv: int, d: int, dtype: str = "bf16",
     if with_do:
         out["do"] = draw((b, n, hq, d), dtype, cfg_id, n, "do", seed)
     return out
+
+
+def make_block_mask(mask_heads: int, n: int, density: float, cfg_id: int = 0, seed: int = 0,
+                    block: int = 128, diagonal: bool = True) -> np.ndarray:
+    """Seeded block mask, uint8 [mask_heads, nb, nb] with nb = ceil(n / block):
+    each entry is 1 with probability ``density``; ``diagonal`` also sets every
+    diagonal block (each query block then sees its own keys)."""
+    nb = -(-n // block)
+    rng = np.random.default_rng(np.random.SeedSequence([int(cfg_id), int(n), TENSOR_ID["mask"], int(seed)]))
+    m = (rng.random((mask_heads, nb, nb)) < density).astype(np.uint8)
+    if diagonal:
+        m[:, np.arange(nb), np.arange(nb)] = 1
+    return m
 
 
 def to_torch(x: np.ndarray, dtype: str, device="cpu"):

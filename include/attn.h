@@ -135,6 +135,47 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, cons
                 size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
                 int causal, float scale, void* stream);
 
+/*
+ * Block-sparse attention.  The FlashAttention-1 news page benchmarks a
+ * block-sparse variant of the method beside the dense one (its paragraph on
+ * runtime and memory against the A100 baselines); the pages do not define
+ * it, and this library reads it as follows.  The key/query positions are cut
+ * into blocks of ATTN_SPARSE_BLOCK, nb = ceil(N / ATTN_SPARSE_BLOCK) per
+ * sequence, and a block mask says which (query block, key block) pairs are
+ * computed: query i may attend key j only if
+ *     block_mask[m][i / ATTN_SPARSE_BLOCK][j / ATTN_SPARSE_BLOCK] != 0
+ * (and j <= i when `causal`, which still drops every block past the
+ * diagonal).  Pairs whose entry is zero are never loaded or computed.
+ *
+ *   block_mask   device memory, uint8 [mask_heads, nb, nb], row-major
+ *                (query block major), read-only, any alignment; it must
+ *                stay unchanged until the stream has run the call
+ *   mask_heads   1: one mask for every batch and head; Hkv: query head h
+ *                uses mask m = h / (Hq / Hkv), the one of its K/V head, so
+ *                all query heads of a GQA group share a pattern
+ *
+ * A query row with no allowed key gets o = 0 and lse = -inf, and in the
+ * backward pass dq = 0 with no contribution to dk or dv.  Everything else
+ * (layouts, dtypes, scale, ownership, asynchrony, error behaviour) is that of
+ * attn_fwd / attn_bwd; additionally block_mask NULL gives ATTN_ERR_NULLPTR, a
+ * mask_heads other than 1 or Hkv ATTN_ERR_SHAPE, and N > ATTN_SPARSE_MAX_N
+ * ATTN_ERR_TOO_LARGE.  attn_bwd_blocksparse takes the same workspace as
+ * attn_bwd and must be given the lse of attn_fwd_blocksparse with the same
+ * mask, causal flag and scale.
+ */
+#define ATTN_SPARSE_BLOCK 128
+#define ATTN_SPARSE_MAX_N 262144
+
+int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                         const unsigned char* block_mask, int mask_heads, int B, int N, int Hq,
+                         int Hkv, int d, int dtype, int causal, float scale, void* stream);
+
+int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
+                         const void* dout, const float* lse, const unsigned char* block_mask,
+                         int mask_heads, void* dq, void* dk, void* dv, void* workspace,
+                         size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
+                         int causal, float scale, void* stream);
+
 /* Static, human-readable description of a status code. */
 const char* attn_strerror(int status);
 

@@ -34,13 +34,16 @@ def run_fwd(x, dtype, causal, scale, device):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def run_fwd_bwd(x, dtype, causal, scale, device):
+def run_fwd_bwd(x, dtype, causal, scale, device, block_mask=None):
+    """Forward then backward through the C ABI; ``block_mask`` (numpy uint8
+    [1 or Hkv, nb, nb]) selects the block-sparse entry points."""
     import torch
     import exact_io_aware_75_amd as ea
 
     q, k, v, do = (upload(x[t], dtype, device) for t in ("q", "k", "v", "do"))
-    o, lse = ea.forward(q, k, v, causal=causal, scale=scale)
-    dq, dk, dv = ea.backward(q, k, v, o, lse, do, causal=causal, scale=scale)
+    bm = None if block_mask is None else torch.from_numpy(np.ascontiguousarray(block_mask, dtype=np.uint8)).to(device)
+    o, lse = ea.forward(q, k, v, causal=causal, scale=scale, block_mask=bm)
+    dq, dk, dv = ea.backward(q, k, v, o, lse, do, causal=causal, scale=scale, block_mask=bm)
     torch.cuda.synchronize()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     return f(o), lse.cpu().numpy().astype(np.float64), f(dq), f(dk), f(dv)

@@ -141,3 +141,20 @@ def test_valid_call_without_gpu_reports_device_error():
     r = subprocess.run(["python", "-c", code], capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     assert int(r.stdout.strip().splitlines()[-1]) == _status_codes()["ATTN_ERR_DEVICE"]
+
+
+def test_blocksparse_rejects_invalid_arguments(lib):
+    c = _status_codes()
+    fwd = lambda mask=A, mh=1, N=128, Hkv=2: lib.attn_fwd_blocksparse(  # noqa: E731
+        A, A, A, A, A, mask, mh, 1, N, 2, Hkv, 64, 1, 0, 0.125, None)
+    assert fwd(mask=None) == c["ATTN_ERR_NULLPTR"]
+    assert fwd(mh=0) == c["ATTN_ERR_SHAPE"]
+    assert fwd(mh=3) == c["ATTN_ERR_SHAPE"]
+    assert fwd(mh=2, Hkv=1) == c["ATTN_ERR_SHAPE"]
+    assert fwd(N=(1 << 18) + 1) == c["ATTN_ERR_TOO_LARGE"]
+    ws = lib.attn_bwd_workspace_bytes(1, 128, 2, 2, 64)
+    bwd = lambda mask=A, mh=2, ws_bytes=ws: lib.attn_bwd_blocksparse(  # noqa: E731
+        A, A, A, A, A, A, mask, mh, A, A, A, A, ws_bytes, 1, 128, 2, 2, 64, 1, 1, 0.125, None)
+    assert bwd(mask=None) == c["ATTN_ERR_NULLPTR"]
+    assert bwd(mh=4) == c["ATTN_ERR_SHAPE"]
+    assert bwd(ws_bytes=ws - 1) == c["ATTN_ERR_WORKSPACE"]

@@ -1,0 +1,169 @@
+"""GPU parity of block-sparse attention (attn_fwd_blocksparse and
+attn_bwd_blocksparse through the C ABI) against the CPU fp64 oracle with the
+same block mask.
+
+Block-sparse attention is the variant the FlashAttention-1 news page
+benchmarks beside the dense method; a block mask over (query block, key
+block) pairs of 128 x 128 says which pairs are computed (AND-ed with the
+causal mask), and a row with no allowed key gets O = 0, LSE = -inf, dQ = 0.
+
+Small shapes: every element of O, LSE, dQ, dK, dV, with masks that leave
+whole query blocks and key blocks empty, ragged last blocks, GQA/MQA with
+shared and per-K/V-head masks, fp16 and bf16, d = 64 / 128 / 256.  Exact
+special cases: an all-ones mask and (under a causal mask) the lower block
+triangle reproduce the dense kernels bitwise, because every wavefront then
+visits the same key tiles in the same order.  Full size: the block-sparse
+benchmark workload on sampled rows and one whole K/V head.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+from exact_io_aware_75_amd import configs
+from exact_io_aware_75_amd import inputs as gen
+from gpu_util import TOL_GRAD, TOL_LSE, TOL_O, excess, log, max_err, run_fwd_bwd
+
+pytestmark = pytest.mark.gpu
+
+BLOCK = 128
+
+
+def _mask(mh, n, seed, empty_row=True, empty_col=True):
+    m = gen.make_block_mask(mh, n, 0.5, cfg_id=31, seed=seed, diagonal=False)
+    nb = m.shape[1]
+    if empty_row and nb > 1:
+        m[:, 1, :] = 0  # query block 1 has no allowed key
+    if empty_col and nb > 2:
+        m[:, :, 2] = 0  # key block 2 is never used
+    return m
+
+
+def _check(x, out, mask, causal, scale, tag, dtype):
+    o, lse, dq, dk, dv = out
+    ro, rlse = oracle.attention_fwd(x["q"], x["k"], x["v"], causal, scale, block_mask=mask, block=BLOCK)
+    rdq, rdk, rdv = oracle.attention_bwd(x["q"], x["k"], x["v"], x["do"], causal, scale,
+                                         block_mask=mask, block=BLOCK)
+    fin = np.isfinite(rlse)
+    errs = {n: max_err(a, r) for n, a, r in (("o", o, ro), ("lse", lse[fin], rlse[fin]), ("dq", dq, rdq),
+                                             ("dk", dk, rdk), ("dv", dv, rdv))}
+    log(f"{tag}: " + "  ".join(f"{n}={e:.2e}(|ref| {m:.2f})" for n, (e, m) in errs.items())
+        + f"  empty rows {int((~fin).sum())}")
+    for t in (o, dq, dk, dv):
+        assert np.isfinite(t).all()
+    assert np.array_equal(np.isfinite(lse), fin) and (lse[~fin] == -np.inf).all()
+    assert excess(o, ro, TOL_O, dtype) <= 0, (tag, "o", errs["o"])
+    assert errs["lse"][0] <= TOL_LSE
+    for n, a_, r_ in (("dq", dq, rdq), ("dk", dk, rdk), ("dv", dv, rdv)):
+        assert excess(a_, r_, TOL_GRAD, dtype) <= 0, (tag, n, errs[n])
+    # rows with no allowed key: exactly zero output and gradient
+    rows = np.transpose(np.nonzero(~fin))  # (b, h, i)
+    for bi, h, i in rows:
+        assert (o[bi, i, h] == 0).all() and (dq[bi, i, h] == 0).all()
+
+
+SMALL = [
+    # b, n, hq, hkv, d, mask heads, dtype
+    (1, 300, 2, 2, 128, 1, "bf16"),
+    (2, 513, 4, 2, 64, 2, "bf16"),
+    (1, 1000, 4, 1, 128, 1, "fp16"),
+    (1, 384, 2, 2, 256, 2, "bf16"),
+    (1, 129, 2, 2, 64, 1, "bf16"),
+    (1, 700, 4, 4, 256, 4, "fp16"),
+    (1, 640, 8, 2, 128, 2, "bf16"),
+]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("b,n,hq,hkv,d,mh,dtype", SMALL)
+def test_small_shapes(gpu_device, b, n, hq, hkv, d, mh, dtype, causal):
+    x = gen.make_inputs(b, n, hq, hkv, d, dtype, cfg_id=31, seed=n)
+    mask = _mask(mh, n, seed=n + d)
+    scale = 1.0 / np.sqrt(d)
+    tag = f"sparse b{b} n{n} hq{hq} hkv{hkv} d{d} masks{mh} {dtype} causal={causal} density={mask.mean():.2f}"
+    log(tag)
+    out = run_fwd_bwd(x, dtype, causal, scale, gpu_device, block_mask=mask)
+    _check(x, out, mask, causal, scale, tag, dtype)
+
+
+@pytest.mark.parametrize("n,d", [(300, 64), (1000, 128), (520, 256)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_mask_equals_dense_bitwise(gpu_device, n, d, causal):
+    x = gen.make_inputs(1, n, 4, 2, d, "bf16", cfg_id=32, seed=n)
+    nb = -(-n // BLOCK)
+    ones = np.ones((1, nb, nb), dtype=np.uint8)
+    log(f"all-ones mask n{n} d{d} causal={causal}")
+    a = run_fwd_bwd(x, "bf16", causal, 1.0 / np.sqrt(d), gpu_device, block_mask=ones)
+    b = run_fwd_bwd(x, "bf16", causal, 1.0 / np.sqrt(d), gpu_device)
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+
+
+def test_lower_block_triangle_is_causal_bitwise(gpu_device):
+    n, d = 777, 128
+    x = gen.make_inputs(2, n, 4, 4, d, "bf16", cfg_id=33)
+    nb = -(-n // BLOCK)
+    tril = np.tril(np.ones((nb, nb), dtype=np.uint8))[None].repeat(4, axis=0)
+    log("lower block triangle, causal")
+    a = run_fwd_bwd(x, "bf16", True, 1.0 / np.sqrt(d), gpu_device, block_mask=tril)
+    b = run_fwd_bwd(x, "bf16", True, 1.0 / np.sqrt(d), gpu_device)
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_empty_mask(gpu_device, causal):
+    x = gen.make_inputs(1, 257, 2, 1, 64, "bf16", cfg_id=34)
+    zero = np.zeros((1, 3, 3), dtype=np.uint8)
+    log(f"empty mask causal={causal}")
+    o, lse, dq, dk, dv = run_fwd_bwd(x, "bf16", causal, 0.125, gpu_device, block_mask=zero)
+    assert (o == 0).all() and (lse == -np.inf).all()
+    assert (dq == 0).all() and (dk == 0).all() and (dv == 0).all()
+
+
+def test_mask_upper_blocks_ignored_when_causal(gpu_device):
+    """Under a causal mask, entries above the block diagonal change nothing."""
+    n, d = 600, 64
+    x = gen.make_inputs(1, n, 2, 2, d, "bf16", cfg_id=35)
+    m = _mask(1, n, seed=5, empty_row=False, empty_col=False)
+    full_upper = m.copy()
+    nb = m.shape[1]
+    full_upper[0][np.triu_indices(nb, 1)] = 1
+    a = run_fwd_bwd(x, "bf16", True, 0.125, gpu_device, block_mask=m)
+    b = run_fwd_bwd(x, "bf16", True, 0.125, gpu_device, block_mask=full_upper)
+    for u, w in zip(a, b):
+        assert np.array_equal(u, w)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_full_size(gpu_device, causal):
+    """The block-sparse benchmark workload (N = 16384, H = 16, d = 128)."""
+    s = configs.blocksparse(causal)
+    x = gen.make_inputs(s.b, s.n, s.hq, s.hkv, s.d, s.dtype, cfg_id=s.cfg_id)
+    mask = gen.make_block_mask(1, s.n, configs.BLOCKSPARSE_DENSITY, cfg_id=s.cfg_id)
+    scale = 1.0 / np.sqrt(s.d)
+    log(f"full-size block-sparse fwd+bwd {s} density {mask.mean():.3f}")
+    o, lse, dq, dk, dv = run_fwd_bwd(x, s.dtype, causal, scale, gpu_device, block_mask=mask)
+    for t in (o, lse, dq, dk, dv):
+        assert np.isfinite(t).all()
+    rng = np.random.default_rng(7 + int(causal))
+    worst = {"o": -1.0, "lse": 0.0, "dq": -1.0}
+    for _ in range(16):
+        bi, h, i = int(rng.integers(s.b)), int(rng.integers(s.hq)), int(rng.integers(s.n))
+        ro, rlse = oracle.attention_head_fwd(x["q"][bi, :, h], x["k"][bi, :, h], x["v"][bi, :, h], causal,
+                                             scale, rows=[i], head_mask=mask[0], block=BLOCK)
+        rdq, _, _ = oracle.attention_head_bwd(x["q"][bi, :, h], x["k"][bi, :, h], x["v"][bi, :, h],
+                                              x["do"][bi, :, h], causal, scale, rows=[i],
+                                              head_mask=mask[0], block=BLOCK)
+        worst["o"] = max(worst["o"], excess(o[bi, i, h], ro[0], TOL_O, s.dtype))
+        worst["lse"] = max(worst["lse"], abs(lse[bi, h, i] - rlse[0]))
+        worst["dq"] = max(worst["dq"], excess(dq[bi, i, h], rdq[0], TOL_GRAD, s.dtype))
+    log(f"  sampled rows: excess o {worst['o']:.2e}, lse err {worst['lse']:.2e}, excess dq {worst['dq']:.2e}")
+    assert worst["o"] <= 0 and worst["lse"] <= TOL_LSE and worst["dq"] <= 0
+    # dK / dV of one whole head (the oracle visits every row once)
+    h = int(rng.integers(s.hq))
+    _, rdk, rdv = oracle.attention_head_bwd(x["q"][0, :, h], x["k"][0, :, h], x["v"][0, :, h],
+                                            x["do"][0, :, h], causal, scale, head_mask=mask[0], block=BLOCK)
+    log(f"  head {h}: max|ddK|={max_err(dk[0, :, h], rdk)[0]:.3e} max|ddV|={max_err(dv[0, :, h], rdv)[0]:.3e}")
+    assert excess(dk[0, :, h], rdk, TOL_GRAD, s.dtype) <= 0
+    assert excess(dv[0, :, h], rdv, TOL_GRAD, s.dtype) <= 0
