@@ -16,7 +16,13 @@ Prints one JSON line.  Besides the throughput it carries
                 bytes per launch measured with rocprofv3 counters for the current
                 kernel source (null when the source changed since);
   cpu_baseline  the CPU fp64 oracle timed on a bounded sample of the same
-                workload on this host.
+                workload on this host;
+  blocksparse   block-sparse attention (attn_fwd_blocksparse /
+                attn_bwd_blocksparse) on its own workload -- hidden 2048,
+                d = 128, B = 1, N = 16384, one block mask with every diagonal
+                block and a seeded 25% of the others -- timed outside the step:
+                TFLOP/s over the computed blocks and the speed-up over the
+                dense kernels on the same shape.
 --sweep also prints per-workload forward/backward TFLOP/s for every full-size
 configuration to stderr.
 """
@@ -207,6 +213,8 @@ def run(args):
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in mean.items()},
         "roofline": roofline,
     }
+    if args.sparse:
+        line["blocksparse"] = blocksparse_measure()
     if args.sweep:
         sweep()
     if args.cpu_seconds > 0:
@@ -264,6 +272,72 @@ def sweep():
               file=sys.stderr, flush=True)
         del q, k, v, do, o, lse, dq, dk, dv, ws
         torch.cuda.empty_cache()
+
+
+def _median_ms(fn, stream, reps=10):
+    import numpy as np
+    import torch
+
+    for _ in range(3):
+        fn()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return float(np.median(ts))
+
+
+def blocksparse_measure():
+    """Block-sparse forward / backward on the block-sparse workload, against
+    the dense kernels on the same shape (HIP events, median of 10)."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_75_amd as ea
+    from exact_io_aware_75_amd import configs
+    from exact_io_aware_75_amd import inputs as gen
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    s0 = configs.blocksparse(False)
+    mask_np = gen.make_block_mask(1, s0.n, configs.BLOCKSPARSE_DENSITY, cfg_id=s0.cfg_id)
+    mask = torch.from_numpy(mask_np).to(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    mk = lambda hh: torch.randn(s0.b, s0.n, hh, s0.d, device=dev, generator=g).to(torch.bfloat16)  # noqa: E731
+    q, k, v, do = mk(s0.hq), mk(s0.hkv), mk(s0.hkv), mk(s0.hq)
+    o, lse = torch.empty_like(q), torch.empty((s0.b, s0.hq, s0.n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(s0.b, s0.n, s0.hq, s0.hkv, s0.d), dtype=torch.uint8, device=dev)
+    sc = 1.0 / float(np.sqrt(s0.d))
+    out = {"workload": f"{s0.name}: B={s0.b} N={s0.n} H={s0.hq} d={s0.d} bf16, 128x128 blocks",
+           "mask": f"diagonal + seeded {configs.BLOCKSPARSE_DENSITY:.0%} of the other blocks, shared by all heads",
+           "density": round(float(mask_np.mean()), 4), "unit": "TFLOP/s (computed blocks only)"}
+    for causal in (False, True):
+        s = configs.blocksparse(causal)
+        fl = configs.masked_fwd_flops(s, mask_np)
+        t = {}
+        for kind, bm in (("sparse", mask), ("dense", None)):
+            t[f"fwd_{kind}"] = _median_ms(lambda: ea.attn_fwd(q, k, v, o, lse, causal, sc, stream, block_mask=bm), stream)
+            t[f"bwd_{kind}"] = _median_ms(lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, causal, sc,
+                                                              stream, block_mask=bm), stream)
+        tag = "causal" if causal else "noncausal"
+        out[tag] = {
+            "flop_fraction": round(fl / s.fwd_flops(), 4),
+            "fwd_ms": round(t["fwd_sparse"], 4), "bwd_ms": round(t["bwd_sparse"], 4),
+            "fwd_tflops": round(fl / (t["fwd_sparse"] / 1e3) / 1e12, 1),
+            "bwd_tflops": round(2.5 * fl / (t["bwd_sparse"] / 1e3) / 1e12, 1),
+            "dense_fwd_ms": round(t["fwd_dense"], 4), "dense_bwd_ms": round(t["bwd_dense"], 4),
+            "speedup_fwd": round(t["fwd_dense"] / t["fwd_sparse"], 2),
+            "speedup_bwd": round(t["bwd_dense"] / t["bwd_sparse"], 2),
+        }
+    del q, k, v, do, o, lse, dq, dk, dv, ws, mask
+    torch.cuda.empty_cache()
+    return out
 
 
 COPY_BYTES = 512 << 20  # calibration copy: reads and writes this many bytes per launch
@@ -372,7 +446,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
             conf = ek["SQ_LDS_BANK_CONFLICT"] / max(1.0, ek["SQ_LDS_IDX_ACTIVE"])
         lines.append(f"{short(nm)[:52]:52s} {r['Calls']:>5s} {avg_us:9.2f} {float(r['Percentage']):6.2f} "
                      f"{rd / 1e6:10.1f} {wr / 1e6:10.1f} {gbs:9.1f} {busy:9.3f} {tf:10.4f} {conf:9.4f}")
-        if "attn_bwd_dkdv_kernel" in nm and ("128, false" in nm or "Li128ELb0E" in nm):
+        if "attn_bwd_dkdv_kernel" in nm and ("128, false, false>" in nm or "Li128ELb0ELb0E" in nm):
             dom = (nm, rd, wr, fk.get("FETCH_SIZE"), wk.get("WRITE_SIZE"), avg_us)
     if dom is None:
         raise SystemExit("dK/dV kernel (d=128, non-causal) not found in the trace")
@@ -397,6 +471,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline budget in seconds (0 disables it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sparse", dest="sparse", action="store_false",
+                    help="skip the block-sparse measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain copy of known size first (for counter calibration)")
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "EVIDENCE_DIR"),
