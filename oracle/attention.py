@@ -41,6 +41,15 @@ with block = 128 rows by 128 keys on the GPU; every other formula is
 unchanged.  A row whose allowed set is empty gets O = 0, LSE = -inf and
 dQ = 0, and adds nothing to dK or dV.
 
+Rectangular attention (Nq queries, Nk keys; the shard shape of a sequence
+split across devices) with a causal offset: query i may attend key j iff
+    j <= i + offset,
+by default offset = Nk - Nq, which aligns the last query with the last key
+(for Nq = Nk the usual causal mask).  Rows whose i + offset is negative have
+no allowed key.  Each device's partial results for one query shard combine
+exactly through their LSEs: LSE = ln sum_p exp(LSE_p) and
+O = sum_p exp(LSE_p - LSE) O_p.
+
 Readings where the pages are silent (listed again in the design doc):
   * causal orientation: query i may attend key j iff j <= i (the pages only
     say the masked triangle is skipped rather than computed and zeroed;
@@ -71,18 +80,19 @@ def kv_head_of(h: int, hq: int, hkv: int) -> int:
     return h // (hq // hkv)
 
 
-def _allowed(rows: np.ndarray, n_keys: int, causal: bool, head_mask=None, block: int = 128) -> np.ndarray:
+def _allowed(rows: np.ndarray, n_keys: int, causal: bool, head_mask=None, block: int = 128,
+             offset: int = 0) -> np.ndarray:
     """Boolean [len(rows), n_keys] mask: key j visible to query row i.
 
-    ``head_mask`` (optional, [ceil(Nq / block), ceil(Nk / block)]) is the
-    block mask of the head: key j is visible only if its (row block, key
-    block) entry is nonzero.
+    Causal: j <= i + offset.  ``head_mask`` (optional, [ceil(Nq / block),
+    ceil(Nk / block)]) is the block mask of the head: key j is visible only if
+    its (row block, key block) entry is nonzero.
     """
     cols = np.arange(n_keys)
     if not causal:
         ok = np.ones((len(rows), n_keys), dtype=bool)
     else:
-        ok = cols[None, :] <= rows[:, None]
+        ok = cols[None, :] <= rows[:, None] + offset
     if head_mask is not None:
         hm = np.asarray(head_mask) != 0
         ok = ok & hm[rows[:, None] // block, cols[None, :] // block]
@@ -106,39 +116,48 @@ def _row_softmax(s: np.ndarray, allowed: np.ndarray):
     return p, lse
 
 
-def attention_head_probs(q, k, causal: bool, scale: float, head_mask=None, block: int = 128) -> np.ndarray:
+def _offset(causal_offset, n_q: int, n_k: int) -> int:
+    """Causal offset: default Nk - Nq (last query aligned with last key)."""
+    return n_k - n_q if causal_offset is None else int(causal_offset)
+
+
+def attention_head_probs(q, k, causal: bool, scale: float, head_mask=None, block: int = 128,
+                         causal_offset=None) -> np.ndarray:
     """Full probability matrix P [Nq, Nk] of one head (small inputs only)."""
     q = np.asarray(q, dtype=_F)
     k = np.asarray(k, dtype=_F)
     s = scale * (q @ k.T)
-    p, _ = _row_softmax(s, _allowed(np.arange(q.shape[0]), k.shape[0], causal, head_mask, block))
+    off = _offset(causal_offset, q.shape[0], k.shape[0])
+    p, _ = _row_softmax(s, _allowed(np.arange(q.shape[0]), k.shape[0], causal, head_mask, block, off))
     return p
 
 
 def attention_head_fwd(q, k, v, causal: bool, scale: float, rows=None, chunk: int = 512,
-                       head_mask=None, block: int = 128):
+                       head_mask=None, block: int = 128, causal_offset=None):
     """O and LSE of one head for the query ``rows`` (default: all rows).
 
-    q: [N, d] all query rows of the head; k, v: [N, d] of its K/V head;
-    head_mask: optional block mask of the head (see ``_allowed``).
+    q: [Nq, d] all query rows of the head; k, v: [Nk, d] of its K/V head;
+    head_mask: optional block mask of the head (see ``_allowed``);
+    causal_offset: see ``_allowed`` (default Nk - Nq).
     Rows are independent, so they are processed in chunks of whole rows.
     """
     q = np.asarray(q, dtype=_F)
     k = np.asarray(k, dtype=_F)
     v = np.asarray(v, dtype=_F)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    off = _offset(causal_offset, q.shape[0], k.shape[0])
     o = np.empty((len(rows), v.shape[1]), dtype=_F)
     lse = np.empty(len(rows), dtype=_F)
     for c0 in range(0, len(rows), chunk):
         r = rows[c0:c0 + chunk]
         s = scale * (q[r] @ k.T)
-        p, lse[c0:c0 + chunk] = _row_softmax(s, _allowed(r, k.shape[0], causal, head_mask, block))
+        p, lse[c0:c0 + chunk] = _row_softmax(s, _allowed(r, k.shape[0], causal, head_mask, block, off))
         o[c0:c0 + chunk] = p @ v
     return o, lse
 
 
 def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk: int = 512,
-                       head_mask=None, block: int = 128):
+                       head_mask=None, block: int = 128, causal_offset=None):
     """Gradients of L = sum(O * dO) for one query head.
 
     Returns (dq_rows, dk, dv): dq for the query ``rows`` (default: all) and this
@@ -151,13 +170,14 @@ def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk
     do = np.asarray(do, dtype=_F)
     full = rows is None
     rows = np.arange(q.shape[0]) if full else np.asarray(rows, dtype=np.int64)
+    off = _offset(causal_offset, q.shape[0], k.shape[0])
     dq = np.empty((len(rows), q.shape[1]), dtype=_F)
     dk = np.zeros_like(k) if full else None
     dv = np.zeros_like(v) if full else None
     for c0 in range(0, len(rows), chunk):
         r = rows[c0:c0 + chunk]
         s = scale * (q[r] @ k.T)
-        p, _ = _row_softmax(s, _allowed(r, k.shape[0], causal, head_mask, block))
+        p, _ = _row_softmax(s, _allowed(r, k.shape[0], causal, head_mask, block, off))
         dp = do[r] @ v.T
         dsum = (p * dp).sum(axis=1)
         ds = p * (dp - dsum[:, None])
@@ -169,12 +189,13 @@ def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk
 
 
 def _check_shapes(q, k, v):
+    """(B, Nq, Nk, Hq, Hkv, d) of q [B,Nq,Hq,d] and k, v [B,Nk,Hkv,d]."""
     if q.ndim != 4 or k.shape != v.shape or k.ndim != 4:
-        raise ValueError("expected q [B,N,Hq,d] and k, v [B,N,Hkv,d]")
-    b, n, hq, d = q.shape
-    if k.shape[0] != b or k.shape[1] != n or k.shape[3] != d:
-        raise ValueError("q and k/v disagree in B, N or d")
-    return b, n, hq, k.shape[2], d
+        raise ValueError("expected q [B,Nq,Hq,d] and k, v [B,Nk,Hkv,d]")
+    b, nq, hq, d = q.shape
+    if k.shape[0] != b or k.shape[3] != d:
+        raise ValueError("q and k/v disagree in B or d")
+    return b, nq, k.shape[1], hq, k.shape[2], d
 
 
 def _head_masks(block_mask, n: int, hkv: int, block: int):
@@ -190,9 +211,13 @@ def _head_masks(block_mask, n: int, hkv: int, block: int):
     return lambda g: m[0] if m.shape[0] == 1 else m[g]
 
 
-def attention_fwd(q, k, v, causal: bool, scale: float, block_mask=None, block: int = 128):
-    """O [B,N,Hq,d] and LSE [B,Hq,N] in float64 (optionally block-sparse)."""
-    b, n, hq, hkv, d = _check_shapes(q, k, v)
+def attention_fwd(q, k, v, causal: bool, scale: float, block_mask=None, block: int = 128,
+                  causal_offset=None):
+    """O [B,Nq,Hq,d] and LSE [B,Hq,Nq] in float64 (optionally block-sparse,
+    which needs Nq = Nk; optionally rectangular with a causal offset)."""
+    b, n, nk, hq, hkv, d = _check_shapes(q, k, v)
+    if block_mask is not None and nk != n:
+        raise ValueError("a block mask needs Nq = Nk")
     mask_of = _head_masks(block_mask, n, hkv, block)
     o = np.empty((b, n, hq, d), dtype=_F)
     lse = np.empty((b, hq, n), dtype=_F)
@@ -201,23 +226,26 @@ def attention_fwd(q, k, v, causal: bool, scale: float, block_mask=None, block: i
             g = kv_head_of(h, hq, hkv)
             o[bi, :, h], lse[bi, h] = attention_head_fwd(
                 q[bi, :, h], k[bi, :, g], v[bi, :, g], causal, scale,
-                head_mask=mask_of(g), block=block)
+                head_mask=mask_of(g), block=block, causal_offset=causal_offset)
     return o, lse
 
 
-def attention_bwd(q, k, v, do, causal: bool, scale: float, block_mask=None, block: int = 128):
+def attention_bwd(q, k, v, do, causal: bool, scale: float, block_mask=None, block: int = 128,
+                  causal_offset=None):
     """(dQ, dK, dV) in float64; dK/dV sum the contributions of each group."""
-    b, n, hq, hkv, d = _check_shapes(q, k, v)
+    b, n, nk, hq, hkv, d = _check_shapes(q, k, v)
+    if block_mask is not None and nk != n:
+        raise ValueError("a block mask needs Nq = Nk")
     mask_of = _head_masks(block_mask, n, hkv, block)
     dq = np.empty((b, n, hq, d), dtype=_F)
-    dk = np.zeros((b, n, hkv, d), dtype=_F)
-    dv = np.zeros((b, n, hkv, d), dtype=_F)
+    dk = np.zeros((b, nk, hkv, d), dtype=_F)
+    dv = np.zeros((b, nk, hkv, d), dtype=_F)
     for bi in range(b):
         for h in range(hq):
             g = kv_head_of(h, hq, hkv)
             dqh, dkh, dvh = attention_head_bwd(
                 q[bi, :, h], k[bi, :, g], v[bi, :, g], do[bi, :, h], causal, scale,
-                head_mask=mask_of(g), block=block)
+                head_mask=mask_of(g), block=block, causal_offset=causal_offset)
             dq[bi, :, h] = dqh
             dk[bi, :, g] += dkh
             dv[bi, :, g] += dvh

@@ -276,7 +276,7 @@ def test_bf16_rounding_is_nearest_even():
 # ---- planted mistakes: each mutated oracle must fail at least one pin ----
 
 def _bwd_mutant(kind):
-    def bwd(q, k, v, do, causal, scale, rows=None, chunk=512, head_mask=None, block=128):
+    def bwd(q, k, v, do, causal, scale, rows=None, chunk=512, head_mask=None, block=128, causal_offset=None):
         q, k, v, do = (np.asarray(t, dtype=np.float64) for t in (q, k, v, do))
         r = np.arange(q.shape[0])
         s = scale * (q @ k.T)

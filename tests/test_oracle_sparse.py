@@ -213,9 +213,9 @@ def test_mask_shape_is_checked():
 def test_planted_transposed_mask_is_caught(monkeypatch):
     real = oa._allowed
 
-    def transposed(rows, n, causal, head_mask=None, block=128):
+    def transposed(rows, n, causal, head_mask=None, block=128, offset=0):
         hm = None if head_mask is None else np.asarray(head_mask).T
-        return real(rows, n, causal, hm, block)
+        return real(rows, n, causal, hm, block, offset)
 
     monkeypatch.setattr(oa, "_allowed", transposed)
     with pytest.raises(AssertionError):
