@@ -22,6 +22,7 @@ ATTN_DTYPE_BF16 = 1
 # Entry points declared in include/attn.h (checked by the ABI test).
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
            "attn_bwd_workspace_bytes", "attn_fwd_blocksparse", "attn_bwd_blocksparse",
+           "attn_fwd_rect", "attn_bwd_rect",
            "attn_strerror", "attn_last_hip_error", "attn_version")
 SPARSE_BLOCK = 128  # ATTN_SPARSE_BLOCK: rows / keys per block of the block mask
 BWD_STAGES = ("attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq")
@@ -61,6 +62,11 @@ def load_library():
     lib.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, vp, vp, sz,
                                          i, i, i, i, i, i, i, f, vp]
     lib.attn_bwd_blocksparse.restype = i
+    ll = ctypes.c_longlong
+    lib.attn_fwd_rect.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, ll, f, vp]
+    lib.attn_fwd_rect.restype = i
+    lib.attn_bwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, ll, f, vp]
+    lib.attn_bwd_rect.restype = i
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_strerror.argtypes = [i]
@@ -116,9 +122,18 @@ def _check(t, shape, dtype, device, name):
 
 def _dims(q, k):
     if q.dim() != 4 or k.dim() != 4:
-        raise ValueError("q must be [B,N,Hq,d] and k/v [B,N,Hkv,d]")
+        raise ValueError("q must be [B,Nq,Hq,d] and k/v [B,Nk,Hkv,d]")
     b, n, hq, d = q.shape
     return b, n, hq, k.shape[2], d
+
+
+def _rect(n, nk, causal_offset, block_mask):
+    """Whether a call needs the rectangular entry point, and its causal offset."""
+    if nk == n and causal_offset in (None, 0):
+        return False, 0
+    if block_mask is not None:
+        raise ValueError("block-sparse attention needs Nq = Nk and no causal offset")
+    return True, (nk - n) if causal_offset is None else int(causal_offset)
 
 
 def _check_mask(block_mask, n, hkv, device):
@@ -132,20 +147,31 @@ def _check_mask(block_mask, n, hkv, device):
     return int(block_mask.shape[0])
 
 
-def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None, block_mask=None) -> None:
+def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None, block_mask=None,
+             causal_offset=None) -> None:
     """Enqueue the forward pass into preallocated ``o`` and ``lse``.
 
     ``block_mask`` (optional, uint8 [1 or Hkv, nb, nb] on q's device) selects
-    the block-sparse entry point ``attn_fwd_blocksparse``.
+    the block-sparse entry point ``attn_fwd_blocksparse``.  K/V with a
+    different sequence length than q, or an explicit ``causal_offset``
+    (default Nk - Nq), select the rectangular entry point ``attn_fwd_rect``.
     """
     import torch
 
     lib = load_library()
     b, n, hq, hkv, d = _dims(q, k)
-    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, n, hkv, d), "k"),
-                       (v, (b, n, hkv, d), "v"), (o, (b, n, hq, d), "o")):
+    nk = k.shape[1]
+    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, nk, hkv, d), "k"),
+                       (v, (b, nk, hkv, d), "v"), (o, (b, n, hq, d), "o")):
         _check(t, shp, q.dtype, q.device, nm)
     _check(lse, (b, hq, n), torch.float32, q.device, "lse")
+    rect, off = _rect(n, nk, causal_offset, block_mask)
+    if rect:
+        st = lib.attn_fwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), b, n, nk, hq, hkv, d,
+                               _dtype_code(q), int(bool(causal)), off, float(scale), _stream(stream, q.device))
+        if st != 0:
+            raise AttnError(st, "attn_fwd_rect")
+        return
     tail = (b, n, hq, hkv, d, _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
     if block_mask is None:
         st, name = lib.attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), *tail), "attn_fwd"
@@ -162,14 +188,16 @@ def attn_bwd_workspace_bytes(b: int, n: int, hq: int, hkv: int, d: int) -> int:
 
 
 def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: float,
-             stream=None, stage: str = "attn_bwd", block_mask=None) -> None:
+             stream=None, stage: str = "attn_bwd", block_mask=None, causal_offset=None) -> None:
     """Enqueue the backward pass into preallocated ``dq``, ``dk``, ``dv``.
 
     ``workspace`` is a uint8 device tensor of at least
     ``attn_bwd_workspace_bytes(B, N, Hq, Hkv, d)`` bytes.  ``stage`` selects
     the whole pass ("attn_bwd") or one of its stages (``BWD_STAGES``), which
     must then be enqueued in order.  ``block_mask`` (as for ``attn_fwd``)
-    selects ``attn_bwd_blocksparse`` (whole pass only).
+    selects ``attn_bwd_blocksparse`` (whole pass only); K/V of another
+    length than q or a ``causal_offset`` select ``attn_bwd_rect`` (whole pass
+    only, workspace sized for the Nq queries).
     """
     import torch
 
@@ -179,18 +207,27 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: 
         raise ValueError("the block-sparse backward pass has no separate stages")
     lib = load_library()
     b, n, hq, hkv, d = _dims(q, k)
-    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, n, hkv, d), "k"),
-                       (v, (b, n, hkv, d), "v"), (o, (b, n, hq, d), "o"),
+    nk = k.shape[1]
+    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, nk, hkv, d), "k"),
+                       (v, (b, nk, hkv, d), "v"), (o, (b, n, hq, d), "o"),
                        (dout, (b, n, hq, d), "dout"), (dq, (b, n, hq, d), "dq"),
-                       (dk, (b, n, hkv, d), "dk"), (dv, (b, n, hkv, d), "dv")):
+                       (dk, (b, nk, hkv, d), "dk"), (dv, (b, nk, hkv, d), "dv")):
         _check(t, shp, q.dtype, q.device, nm)
+    rect, off = _rect(n, nk, causal_offset, block_mask)
+    if rect and stage != "attn_bwd":
+        raise ValueError("the rectangular backward pass has no separate stages")
     _check(lse, (b, hq, n), torch.float32, q.device, "lse")
     if workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on q's device")
     ws_bytes = workspace.numel() * workspace.element_size()
     tail = (_ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, b, n, hq, hkv, d,
             _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
-    if block_mask is None:
+    if rect:
+        stage = "attn_bwd_rect"
+        st = lib.attn_bwd_rect(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                               _ptr(dv), _ptr(workspace), ws_bytes, b, n, nk, hq, hkv, d, _dtype_code(q),
+                               int(bool(causal)), off, float(scale), _stream(stream, q.device))
+    elif block_mask is None:
         st = getattr(lib, stage)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), *tail)
     else:
         mh = _check_mask(block_mask, n, hkv, q.device)
@@ -205,22 +242,24 @@ def _default_scale(d: int, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def forward(q, k, v, causal: bool = False, scale=None, stream=None, block_mask=None):
-    """Allocate ``o`` and ``lse`` and run ``attn_fwd`` (or, with a block
-    mask, ``attn_fwd_blocksparse``); returns (o, lse)."""
+def forward(q, k, v, causal: bool = False, scale=None, stream=None, block_mask=None, causal_offset=None):
+    """Allocate ``o`` and ``lse`` and run ``attn_fwd`` (with a block mask
+    ``attn_fwd_blocksparse``; with Nk != Nq or a causal offset
+    ``attn_fwd_rect``); returns (o, lse)."""
     import torch
 
     b, n, hq, _, d = _dims(q, k)
     o = torch.empty_like(q)
     lse = torch.empty((b, hq, n), dtype=torch.float32, device=q.device)
-    attn_fwd(q, k, v, o, lse, causal, _default_scale(d, scale), stream, block_mask=block_mask)
+    attn_fwd(q, k, v, o, lse, causal, _default_scale(d, scale), stream, block_mask=block_mask,
+             causal_offset=causal_offset)
     return o, lse
 
 
 def backward(q, k, v, o, lse, dout, causal: bool = False, scale=None, stream=None, workspace=None,
-             block_mask=None):
+             block_mask=None, causal_offset=None):
     """Allocate gradients (and the workspace if not given) and run ``attn_bwd``
-    (or, with a block mask, ``attn_bwd_blocksparse``)."""
+    (or the block-sparse / rectangular entry point, as in ``forward``)."""
     import torch
 
     b, n, hq, hkv, d = _dims(q, k)
@@ -229,5 +268,5 @@ def backward(q, k, v, o, lse, dout, causal: bool = False, scale=None, stream=Non
         workspace = torch.empty(attn_bwd_workspace_bytes(b, n, hq, hkv, d), dtype=torch.uint8,
                                 device=q.device)
     attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal, _default_scale(d, scale), stream,
-             block_mask=block_mask)
+             block_mask=block_mask, causal_offset=causal_offset)
     return dq, dk, dv

@@ -88,11 +88,20 @@ BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int /*Hkv*/, int d) {
 
 namespace {
 
+// Causal offsets beyond [-Nq, Nk] mean the same as these bounds (no row, or
+// every key, visible); clamping keeps row + offset far from int overflow.
+int clamp_offset(long long off, int Nq, int Nk) {
+  return (int)(off < -(long long)Nq ? -(long long)Nq : (off > Nk ? Nk : off));
+}
+
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
-               const unsigned char* block_mask, int mask_heads, int B, int N, int Hq, int Hkv,
-               int d, int dtype, int causal, float scale, void* stream) {
+               const unsigned char* block_mask, int mask_heads, int B, int N, int Nk, int Hq,
+               int Hkv, int d, int dtype, int causal, long long causal_offset, float scale,
+               void* stream) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULLPTR;
   int st = check_shape(B, N, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  st = check_shape(B, Nk, Hq, Hkv, d);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(lse))
@@ -120,6 +129,8 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   a.neg_scale = scale < 0.f ? 1 : 0;
   a.scale_log2 = std::fabs(scale) * 1.4426950408889634f;
   a.sp = sp;
+  a.Nk = Nk;
+  a.coff = clamp_offset(causal_offset, N, Nk);
   hipError_t e = attn::launch_fwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -135,14 +146,21 @@ extern "C" {
 
 int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int N,
              int Hq, int Hkv, int d, int dtype, int causal, float scale, void* stream) {
-  return fwd_common(q, k, v, o, lse, nullptr, 0, B, N, Hq, Hkv, d, dtype, causal, scale, stream);
+  return fwd_common(q, k, v, o, lse, nullptr, 0, B, N, N, Hq, Hkv, d, dtype, causal, 0, scale, stream);
+}
+
+int attn_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Nq,
+                  int Nk, int Hq, int Hkv, int d, int dtype, int causal, long long causal_offset,
+                  float scale, void* stream) {
+  return fwd_common(q, k, v, o, lse, nullptr, 0, B, Nq, Nk, Hq, Hkv, d, dtype, causal, causal_offset,
+                    scale, stream);
 }
 
 int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
                          const unsigned char* block_mask, int mask_heads, int B, int N, int Hq,
                          int Hkv, int d, int dtype, int causal, float scale, void* stream) {
   if (!block_mask) return ATTN_ERR_NULLPTR;
-  return fwd_common(q, k, v, o, lse, block_mask, mask_heads, B, N, Hq, Hkv, d, dtype, causal,
+  return fwd_common(q, k, v, o, lse, block_mask, mask_heads, B, N, N, Hq, Hkv, d, dtype, causal, 0,
                     scale, stream);
 }
 
@@ -155,12 +173,15 @@ size_t attn_bwd_workspace_bytes(int B, int N, int Hq, int Hkv, int d) {
 
 namespace {
 
-int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, const void* q,
-               const void* k, const void* v, const void* o, const void* dout, const float* lse,
-               void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
-               int N, int Hq, int Hkv, int d, int dtype, int causal, float scale, void* stream) {
+int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, int Nk,
+               long long causal_offset, const void* q, const void* k, const void* v, const void* o,
+               const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
+               size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype, int causal,
+               float scale, void* stream) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULLPTR;
   int st = check_shape(B, N, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  st = check_shape(B, Nk, Hq, Hkv, d);
   if (st != ATTN_OK) return st;
   if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
   const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv};
@@ -197,6 +218,8 @@ int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, cons
   a.scale = scale;
   a.scale_log2 = scale * 1.4426950408889634f;
   a.sp = sp;
+  a.Nk = Nk;
+  a.coff = clamp_offset(causal_offset, N, Nk);
   hipError_t e = attn::launch_bwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0, stages,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -219,10 +242,18 @@ extern "C" {
   q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes, B, N, Hq, Hkv, d, dtype,   \
       causal, scale, stream
 
-int attn_bwd(ATTN_BWD_ARGS) { return bwd_common(7, nullptr, 0, ATTN_BWD_PASS); }
-int attn_bwd_preprocess(ATTN_BWD_ARGS) { return bwd_common(1, nullptr, 0, ATTN_BWD_PASS); }
-int attn_bwd_dkdv(ATTN_BWD_ARGS) { return bwd_common(2, nullptr, 0, ATTN_BWD_PASS); }
-int attn_bwd_dq(ATTN_BWD_ARGS) { return bwd_common(4, nullptr, 0, ATTN_BWD_PASS); }
+int attn_bwd(ATTN_BWD_ARGS) { return bwd_common(7, nullptr, 0, N, 0, ATTN_BWD_PASS); }
+int attn_bwd_preprocess(ATTN_BWD_ARGS) { return bwd_common(1, nullptr, 0, N, 0, ATTN_BWD_PASS); }
+int attn_bwd_dkdv(ATTN_BWD_ARGS) { return bwd_common(2, nullptr, 0, N, 0, ATTN_BWD_PASS); }
+int attn_bwd_dq(ATTN_BWD_ARGS) { return bwd_common(4, nullptr, 0, N, 0, ATTN_BWD_PASS); }
+
+int attn_bwd_rect(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, int B, int Nq, int Nk, int Hq, int Hkv, int d, int dtype,
+                  int causal, long long causal_offset, float scale, void* stream) {
+  return bwd_common(7, nullptr, 0, Nk, causal_offset, q, k, v, o, dout, lse, dq, dk, dv, workspace,
+                    workspace_bytes, B, Nq, Hq, Hkv, d, dtype, causal, scale, stream);
+}
 
 int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void* o,
                          const void* dout, const float* lse, const unsigned char* block_mask,
@@ -230,7 +261,7 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
                          size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
                          int causal, float scale, void* stream) {
   if (!block_mask) return ATTN_ERR_NULLPTR;
-  return bwd_common(7, block_mask, mask_heads, ATTN_BWD_PASS);
+  return bwd_common(7, block_mask, mask_heads, N, 0, ATTN_BWD_PASS);
 }
 
 #undef ATTN_BWD_ARGS

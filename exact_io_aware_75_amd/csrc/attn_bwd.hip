@@ -277,7 +277,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   const int l32 = lane & 31;
 
   // ---- which (batch, kv head, key block) this workgroup owns ----
-  const int nkb = (a.N + KV_BN - 1) / KV_BN;
+  const int nkb = (a.Nk + KV_BN - 1) / KV_BN;
   const int total = nkb * a.Hkv * a.B;
   const int Lw = xcd_remap(blockIdx.x, total);
   const int bg = Lw / nkb;
@@ -290,14 +290,14 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 
   const int q_row = a.Hq * D;
   const int kv_row = a.Hkv * D;
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.N * a.Hkv + g) * D;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.N * a.Hkv + g) * D;
+  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.Nk * a.Hkv + g) * D;
+  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.Nk * a.Hkv + g) * D;
 
   // K (and V if in registers) as B operands: lane = key, 8 consecutive d per k-step
   frag8_t kf[NKK], vf[V_LDS ? 1 : NKK];
   {
-    const uint16_t* kr = kbase + (size_t)min(mykey, a.N - 1) * kv_row + 8 * half;
-    const uint16_t* vr = vbase + (size_t)min(mykey, a.N - 1) * kv_row + 8 * half;
+    const uint16_t* kr = kbase + (size_t)min(mykey, a.Nk - 1) * kv_row + 8 * half;
+    const uint16_t* vr = vbase + (size_t)min(mykey, a.Nk - 1) * kv_row + 8 * half;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       kf[kk] = *(const frag8_t*)(kr + 16 * kk);
@@ -309,7 +309,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   if (V_LDS) {  // the V block, [key][d], swizzled; read as B operand (lane = key)
     TileDma<D, KV_BN, W> vdma;
     vdma.init(kv_row, wave, lane);
-    vdma.load(vbase + (size_t)k0 * kv_row, a.N - k0, kv_row, vblk);
+    vdma.load(vbase + (size_t)k0 * kv_row, a.Nk - k0, kv_row, vblk);
   }
 
   f32x16_t dk_acc[NDB], dv_acc[NDB];  // dK^T, dV^T: lane = key, rows = d
@@ -320,9 +320,9 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   }
 
   // query tiles: every head of the GQA group x tiles of KV_BM rows
-  // (causal: only tiles with a row >= k0)
+  // (causal: only tiles with a row i that sees key k0, i + coff >= k0)
   const int nqt = (a.N + KV_BM - 1) / KV_BM;
-  const int qt0 = CAUSAL ? k0 / KV_BM : 0;
+  const int qt0 = CAUSAL ? min(nqt, max(0, floor_div(k0 - a.coff, KV_BM))) : 0;
   int tiles_per_head = nqt - qt0;
   // Block-sparse: the query tiles of the listed query blocks (causal: from
   // the diagonal block on), KV_BM rows at a time; only the last block of the
@@ -428,7 +428,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     // P = 2^(S c - LSE2), dS = P (dP - D)
-    const int klim = mykey - q0 - 4 * half;
+    const int klim = mykey - a.coff - q0 - 4 * half;
     u32x4_t pq[2], dsq[2];  // packed P and dS, already the B-operand register tuples
 #pragma unroll
     for (int r4 = 0; r4 < 4; ++r4) {
@@ -512,9 +512,9 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   if (t < ntiles) step(t, 0);
 
   // ---- epilogue: dK = scale * dK_acc, dV = dV_acc; lane = key, rows = d ----
-  if (mykey < a.N) {
-    uint16_t* dkp = (uint16_t*)a.dk + ((size_t)b * a.N * a.Hkv + g) * D + (size_t)mykey * kv_row;
-    uint16_t* dvp = (uint16_t*)a.dv + ((size_t)b * a.N * a.Hkv + g) * D + (size_t)mykey * kv_row;
+  if (mykey < a.Nk) {
+    uint16_t* dkp = (uint16_t*)a.dk + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)mykey * kv_row;
+    uint16_t* dvp = (uint16_t*)a.dv + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)mykey * kv_row;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -628,19 +628,28 @@ attn_bwd_dq_kernel(BwdArgs a) {
   const float dlt = a.delta[li];
   const float c = a.scale_log2;  // scale * log2(e), signed
 
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.N * a.Hkv + g) * D;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.N * a.Hkv + g) * D;
+  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.Nk * a.Hkv + g) * D;
+  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.Nk * a.Hkv + g) * D;
   TileDma<D, BN, W, true> dma;
   dma.init(kv_row, wave, lane);
   FragRd<D> fr;
   fr.init(lane);
 
-  const int ntiles_all = (a.N + BN - 1) / BN;
-  int ntiles = ntiles_all, nwave = ntiles_all, nfull = a.N / BN;
+  // (causal: query i sees keys j <= i + coff)
+  const int ntiles_all = (a.Nk + BN - 1) / BN;
+  int ntiles = ntiles_all, nwave = ntiles_all, nfull = a.Nk / BN;
   if (CAUSAL) {
-    ntiles = min(ntiles_all, (min(row0 + DQ_BM, a.N) - 1) / BN + 1);
-    nwave = min(ntiles_all, (wrow0 + 31) / BN + 1);
-    nfull = min(nfull, (wrow0 + 1) / BN);
+    ntiles = max(0, min(ntiles_all, floor_div(min(row0 + DQ_BM, a.N) - 1 + a.coff, BN) + 1));
+    nwave = max(0, min(ntiles, floor_div(wrow0 + 31 + a.coff, BN) + 1));
+    nfull = max(0, min(min(nfull, ntiles), floor_div(wrow0 + 1 + a.coff, BN)));
+    if (ntiles == 0) {  // an offset can leave every row of the block without a key: dQ = 0
+      if (qrow < a.N) {
+        uint16_t* dqr = (uint16_t*)a.dq + (((size_t)b * a.N + qrow) * a.Hq + h) * D;
+#pragma unroll
+        for (int i = 0; i < D / 16; ++i) *(u32x4_t*)(dqr + 16 * i + 8 * half) = (u32x4_t){0u, 0u, 0u, 0u};
+      }
+      return;
+    }
   }
   if constexpr (SPARSE) {
     // bounds on the key tile index -> counts of loop steps (every listed
@@ -659,8 +668,8 @@ attn_bwd_dq_kernel(BwdArgs a) {
   auto load = [&](int j, uint16_t* ks, uint16_t* vs) {
     const int kt = ktile(j);
     const size_t off = (size_t)kt * BN * kv_row;
-    dma.load(kbase + off, a.N - kt * BN, kv_row, ks);
-    dma.load(vbase + off, a.N - kt * BN, kv_row, vs);
+    dma.load(kbase + off, a.Nk - kt * BN, kv_row, ks);
+    dma.load(vbase + off, a.Nk - kt * BN, kv_row, vs);
   };
 
   auto tile = [&](int j, const uint16_t* ks, const uint16_t* vs, auto mask_tag)
@@ -672,8 +681,8 @@ attn_bwd_dq_kernel(BwdArgs a) {
     const int key0 = MASK ? ktile(j) * BN : 0;
     int lim = 0;
     if (MASK) {
-      lim = a.N - 1 - key0 - 4 * half;
-      if (CAUSAL) lim = min(lim, qrow - key0 - 4 * half);
+      lim = a.Nk - 1 - key0 - 4 * half;
+      if (CAUSAL) lim = min(lim, qrow + a.coff - key0 - 4 * half);
     }
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
@@ -781,7 +790,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   if (SPARSE && (a.sp.bmask == nullptr || a.sp.nb != (a.N + SPARSE_BLOCK - 1) / SPARSE_BLOCK ||
-                 a.sp.nb > SPARSE_MAX_NB))
+                 a.sp.nb > SPARSE_MAX_NB || a.Nk != a.N || a.coff != 0))
     return hipErrorInvalidValue;
   const long long rows = (long long)a.B * a.N * a.Hq;
   if (stages & 1) {
@@ -794,7 +803,7 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   }
   if (stages & 2) {
     constexpr int W = DkdvWG<D, CAUSAL>::WAVES;
-    const long long grid = (long long)((a.N + 32 * W - 1) / (32 * W)) * a.Hkv * a.B;
+    const long long grid = (long long)((a.Nk + 32 * W - 1) / (32 * W)) * a.Hkv * a.B;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W), 0,
                        stream, a);

@@ -108,6 +108,9 @@ __device__ __forceinline__ int compact_mask(const uint8_t* p, int stride, int fi
   return cnt;
 }
 
+// floor(a / b) for b > 0 and any sign of a (causal bounds with an offset).
+__device__ __forceinline__ int floor_div(int a, int b) { return a >= 0 ? a / b : -((b - 1 - a) / b); }
+
 // Wave-uniform read of an LDS list entry (kept in a scalar register).
 __device__ __forceinline__ int lds_uniform(const uint16_t* list, int i) {
   return __builtin_amdgcn_readfirstlane((int)list[i]);

@@ -160,13 +160,22 @@ attn_fwd_kernel(FwdArgs a) {
   const size_t q_row = (size_t)a.Hq * D;   // elements between consecutive query rows
   const size_t kv_row = (size_t)a.Hkv * D;
   const uint16_t* qbase = (const uint16_t*)a.q + ((size_t)b * a.N * a.Hq + h) * D;
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.N * a.Hkv + g) * D;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.N * a.Hkv + g) * D;
+  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.Nk * a.Hkv + g) * D;
+  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.Nk * a.Hkv + g) * D;
 
   const int row0 = rb * FWD_BM;                 // first query row of the workgroup
   const int wrow0 = row0 + wave * 32;           // first query row of this wavefront
   const int qrow = wrow0 + l32;                 // this lane's query row
   const bool qvalid = qrow < a.N;
+  // O = 0 and LSE = -inf for the rows of a workgroup that sees no key at all
+  auto write_empty = [&]() __attribute__((always_inline)) {
+    if (qvalid) {
+      uint16_t* orow = (uint16_t*)a.o + ((size_t)b * a.N * a.Hq + h) * D + (size_t)qrow * q_row;
+#pragma unroll
+      for (int i = 0; i < D / 16; ++i) *(u32x4_t*)(orow + 16 * i + 8 * half) = (u32x4_t){0u, 0u, 0u, 0u};
+      if (half == 0) a.lse[((size_t)b * a.Hq + h) * a.N + qrow] = -INFINITY;
+    }
+  };
 
   // ---- block-sparse: list the allowed key blocks of row block rb ----
   // (causal: blocks past the diagonal are dropped whatever the mask says)
@@ -179,13 +188,8 @@ attn_fwd_kernel(FwdArgs a) {
     }
     __syncthreads();
     nlist = __builtin_amdgcn_readfirstlane(bcount);
-    if (nlist == 0) {  // no allowed key in any row of the block: O = 0, LSE = -inf
-      if (qvalid) {
-        uint16_t* orow = (uint16_t*)a.o + ((size_t)b * a.N * a.Hq + h) * D + (size_t)qrow * q_row;
-#pragma unroll
-        for (int i = 0; i < D / 16; ++i) *(u32x4_t*)(orow + 16 * i + 8 * half) = (u32x4_t){0u, 0u, 0u, 0u};
-        if (half == 0) a.lse[((size_t)b * a.Hq + h) * a.N + qrow] = -INFINITY;
-      }
+    if (nlist == 0) {  // no allowed key in any row of the block
+      write_empty();
       return;
     }
   }
@@ -211,14 +215,19 @@ attn_fwd_kernel(FwdArgs a) {
   const float c = a.scale_log2;  // |scale| * log2(e)
 
   // ---- key tiles: the workgroup's trip count and this wavefront's share ----
-  const int ntiles_all = (a.N + BN - 1) / BN;
+  // (causal: query i sees keys j <= i + coff)
+  const int ntiles_all = (a.Nk + BN - 1) / BN;
   int ntiles = ntiles_all;   // tiles the workgroup streams through LDS
   int nwave = ntiles_all;    // tiles this wavefront computes
-  int nfull = a.N / BN;      // leading tiles that need no element mask
+  int nfull = a.Nk / BN;     // leading tiles that need no element mask
   if (CAUSAL) {
-    ntiles = min(ntiles_all, (min(row0 + FWD_BM, a.N) - 1) / BN + 1);
-    nwave = min(ntiles_all, (wrow0 + 31) / BN + 1);
-    nfull = min(nfull, (wrow0 + 1) / BN);
+    ntiles = max(0, min(ntiles_all, floor_div(min(row0 + FWD_BM, a.N) - 1 + a.coff, BN) + 1));
+    nwave = max(0, min(ntiles, floor_div(wrow0 + 31 + a.coff, BN) + 1));
+    nfull = max(0, min(min(nfull, ntiles), floor_div(wrow0 + 1 + a.coff, BN)));
+    if (ntiles == 0) {  // an offset can leave every row of the block without a key
+      write_empty();
+      return;
+    }
   }
   if constexpr (SPARSE) {
     // The counts above are bounds on the key tile index.  Every listed block
@@ -253,7 +262,7 @@ attn_fwd_kernel(FwdArgs a) {
     const uint16_t* src = base + (size_t)j * BN * kv_row;
     // bytes from the tile's first row to the sequence end: < 2^32, as the host
     // bounds N * H * d below 2^31 elements
-    const uint32_t nrec = (uint32_t)(a.N - j * BN) * (uint32_t)kv_row * 2u;
+    const uint32_t nrec = (uint32_t)(a.Nk - j * BN) * (uint32_t)kv_row * 2u;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)nrec, 0x00020000);
 #pragma unroll
@@ -380,7 +389,7 @@ attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool ok = key < a.N && (!CAUSAL || key <= qrow);
+        const bool ok = key < a.Nk && (!CAUSAL || key <= qrow + a.coff);
         s[sb][r] = ok ? s[sb][r] : -INFINITY;
       }
   };
@@ -518,6 +527,9 @@ attn_fwd_kernel(FwdArgs a) {
                                                      __builtin_bit_cast(uint32_t, ls), false, false);
     ltot = __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
   }
+  // A row with no allowed key (causal, qrow + coff < 0; its accumulators
+  // are not meaningful) gets O = 0 and LSE = -inf; the test is on integers.
+  const bool empty = CAUSAL && qrow + a.coff < 0;
   if (qvalid) {
     const float inv = 1.0f / ltot;
     uint16_t* orow = (uint16_t*)a.o + ((size_t)b * a.N * a.Hq + h) * D + (size_t)qrow * q_row;
@@ -528,11 +540,12 @@ attn_fwd_kernel(FwdArgs a) {
         const int d0 = 32 * db + 8 * q4 + 4 * half;
         u32x2_t w = {pack2(Tag{}, oacc[db][4 * q4 + 0] * inv, oacc[db][4 * q4 + 1] * inv),
                      pack2(Tag{}, oacc[db][4 * q4 + 2] * inv, oacc[db][4 * q4 + 3] * inv)};
+        if (empty) w = (u32x2_t){0u, 0u};
         *(u32x2_t*)(orow + d0) = w;
       }
     if (half == 0) {
       const float lse2 = m_ref + log2f(ltot);
-      a.lse[((size_t)b * a.Hq + h) * a.N + qrow] = lse2 * 0.69314718055994530942f;
+      a.lse[((size_t)b * a.Hq + h) * a.N + qrow] = empty ? -INFINITY : lse2 * 0.69314718055994530942f;
     }
   }
 }
@@ -545,7 +558,8 @@ hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t stream) {
   const int nblk = (a.N + WG::BM - 1) / WG::BM;
   const long long total = (long long)nblk * a.Hq * a.B;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if (SPARSE && (a.sp.bmask == nullptr || a.sp.nb != nblk || a.sp.nb > SPARSE_MAX_NB)) return hipErrorInvalidValue;
+  if (SPARSE && (a.sp.bmask == nullptr || a.sp.nb != nblk || a.sp.nb > SPARSE_MAX_NB || a.Nk != a.N || a.coff != 0))
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)total), dim3(WG::THREADS), 0,
                      stream, a);
   return hipGetLastError();

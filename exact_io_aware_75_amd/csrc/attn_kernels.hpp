@@ -23,11 +23,13 @@ struct SparseArgs {
 
 struct FwdArgs {
   const void* q;  // [B, N, Hq, d]
-  const void* k;  // [B, N, Hkv, d]
-  const void* v;  // [B, N, Hkv, d]
+  const void* k;  // [B, Nk, Hkv, d]
+  const void* v;  // [B, Nk, Hkv, d]
   void* o;        // [B, N, Hq, d]
   float* lse;     // [B, Hq, N]
   int B, N, Hq, Hkv;
+  int Nk;            // keys (K/V rows per sequence); N is the number of queries
+  int coff;          // causal: query i sees key j iff j <= i + coff (clamped to [-N, Nk])
   int group;         // Hq / Hkv
   int neg_scale;     // 1 if scale < 0 (folded into Q's sign)
   float scale_log2;  // |scale| * log2(e)
@@ -46,6 +48,8 @@ struct BwdArgs {
   void* dv;
   float* delta;      // workspace: [B, Hq, N] fp32, rowsum(dO * O)
   int B, N, Hq, Hkv;
+  int Nk;            // keys; N is the number of queries
+  int coff;          // causal offset, as in FwdArgs
   int group;
   float scale;       // signed softmax scale
   float scale_log2;  // scale * log2(e)

@@ -136,6 +136,33 @@ int attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, cons
                 int causal, float scale, void* stream);
 
 /*
+ * Rectangular attention: Nq queries against Nk keys, the shape one device
+ * computes when the sequence is split across devices (the pages parallelise
+ * over the sequence: FlashAttention-2 announcement, section "具体实现";
+ * FlashAttention-2 review, section "Параллелизм").  q, o, dout, dq are
+ * [B, Nq, Hq, d], k, v, dk, dv are [B, Nk, Hkv, d], lse is [B, Hq, Nq]; with
+ * `causal` set, query i attends key j only if
+ *     j <= i + causal_offset
+ * (causal_offset = Nk - Nq aligns the last query with the last key; for a
+ * block of keys that starts at position p of the sequence and queries that
+ * start at position r, causal_offset = r - p).  Rows with no allowed key get
+ * o = 0, lse = -inf and dq = 0.  Partial results over disjoint key blocks
+ * combine exactly: lse = ln sum_p exp(lse_p), o = sum_p exp(lse_p - lse) o_p.
+ * Everything else is that of attn_fwd / attn_bwd; the backward workspace is
+ * attn_bwd_workspace_bytes(B, Nq, Hq, Hkv, d), and attn_fwd_rect(..., Nq = Nk
+ * = N, causal_offset = 0) is attn_fwd.  Offsets outside [-Nq, Nk] act as
+ * these bounds.
+ */
+int attn_fwd_rect(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int Nq, int Nk, int Hq, int Hkv, int d, int dtype, int causal,
+                  long long causal_offset, float scale, void* stream);
+
+int attn_bwd_rect(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                  size_t workspace_bytes, int B, int Nq, int Nk, int Hq, int Hkv, int d,
+                  int dtype, int causal, long long causal_offset, float scale, void* stream);
+
+/*
  * Block-sparse attention.  The FlashAttention-1 news page benchmarks a
  * block-sparse variant of the method beside the dense one (its paragraph on
  * runtime and memory against the A100 baselines); the pages do not define

@@ -34,19 +34,29 @@ def run_fwd(x, dtype, causal, scale, device):
     return o.float().cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
 
 
-def run_fwd_bwd(x, dtype, causal, scale, device, block_mask=None):
+def run_fwd_bwd(x, dtype, causal, scale, device, block_mask=None, causal_offset=None):
     """Forward then backward through the C ABI; ``block_mask`` (numpy uint8
-    [1 or Hkv, nb, nb]) selects the block-sparse entry points."""
+    [1 or Hkv, nb, nb]) selects the block-sparse entry points, K/V longer or
+    shorter than Q or a ``causal_offset`` the rectangular ones."""
     import torch
     import exact_io_aware_75_amd as ea
 
     q, k, v, do = (upload(x[t], dtype, device) for t in ("q", "k", "v", "do"))
     bm = None if block_mask is None else torch.from_numpy(np.ascontiguousarray(block_mask, dtype=np.uint8)).to(device)
-    o, lse = ea.forward(q, k, v, causal=causal, scale=scale, block_mask=bm)
-    dq, dk, dv = ea.backward(q, k, v, o, lse, do, causal=causal, scale=scale, block_mask=bm)
+    o, lse = ea.forward(q, k, v, causal=causal, scale=scale, block_mask=bm, causal_offset=causal_offset)
+    dq, dk, dv = ea.backward(q, k, v, o, lse, do, causal=causal, scale=scale, block_mask=bm,
+                             causal_offset=causal_offset)
     torch.cuda.synchronize()
     f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
     return f(o), lse.cpu().numpy().astype(np.float64), f(dq), f(dk), f(dv)
+
+
+def make_rect_inputs(b, nq, nk, hq, hkv, d, dtype, cfg_id, seed=0):
+    """Q, dO [B,Nq,Hq,d] and K, V [B,Nk,Hkv,d] from the seeded generator."""
+    return {"q": gen.draw((b, nq, hq, d), dtype, cfg_id, nq, "q", seed),
+            "k": gen.draw((b, nk, hkv, d), dtype, cfg_id, nk, "k", seed),
+            "v": gen.draw((b, nk, hkv, d), dtype, cfg_id, nk, "v", seed),
+            "do": gen.draw((b, nq, hq, d), dtype, cfg_id, nq, "do", seed)}
 
 
 def half_ulp(ref, dtype):

@@ -158,3 +158,18 @@ def test_blocksparse_rejects_invalid_arguments(lib):
     assert bwd(mask=None) == c["ATTN_ERR_NULLPTR"]
     assert bwd(mh=4) == c["ATTN_ERR_SHAPE"]
     assert bwd(ws_bytes=ws - 1) == c["ATTN_ERR_WORKSPACE"]
+
+
+def test_rect_rejects_invalid_arguments(lib):
+    c = _status_codes()
+    fwd = lambda Nq=128, Nk=256, off=0, q=A: lib.attn_fwd_rect(  # noqa: E731
+        q, A, A, A, A, 1, Nq, Nk, 2, 2, 64, 1, 1, off, 0.125, None)
+    assert fwd(q=None) == c["ATTN_ERR_NULLPTR"]
+    assert fwd(Nq=0) == c["ATTN_ERR_SHAPE"]
+    assert fwd(Nk=0) == c["ATTN_ERR_SHAPE"]
+    assert fwd(Nk=1 << 24) == c["ATTN_ERR_TOO_LARGE"]
+    ws = lib.attn_bwd_workspace_bytes(1, 128, 2, 2, 64)
+    bwd = lambda ws_bytes=ws, Nk=256: lib.attn_bwd_rect(  # noqa: E731
+        A, A, A, A, A, A, A, A, A, A, ws_bytes, 1, 128, Nk, 2, 2, 64, 1, 1, -(1 << 40), 0.125, None)
+    assert bwd(ws_bytes=ws - 1) == c["ATTN_ERR_WORKSPACE"]
+    assert bwd(Nk=-1) == c["ATTN_ERR_SHAPE"]
