@@ -22,7 +22,14 @@ Prints one JSON line.  Besides the throughput it carries
                 d = 128, B = 1, N = 16384, one block mask with every diagonal
                 block and a seeded 25% of the others -- timed outside the step:
                 TFLOP/s over the computed blocks and the speed-up over the
-                dense kernels on the same shape.
+                dense kernels on the same shape;
+  shard         rectangular attention (attn_fwd_rect / attn_bwd_rect) on one
+                device's share of a causal 65536-token sequence split 8 ways:
+                the last 8192 queries against all 65536 keys, B = 1, H = 8,
+                d = 128 (FLOPs over the allowed query-key pairs); and the
+                split-KV forward (attn_fwd_splitkv) on a short-query shape,
+                128 queries against 65536 keys, B = 1, H = 32, d = 128,
+                against the unsplit kernel.
 --sweep also prints per-workload forward/backward TFLOP/s for every full-size
 configuration to stderr.
 """
@@ -215,6 +222,7 @@ def run(args):
     }
     if args.sparse:
         line["blocksparse"] = blocksparse_measure()
+        line["shard"] = shard_measure()
     if args.sweep:
         sweep()
     if args.cpu_seconds > 0:
@@ -338,6 +346,60 @@ def blocksparse_measure():
     del q, k, v, do, o, lse, dq, dk, dv, ws, mask
     torch.cuda.empty_cache()
     return out
+
+
+def shard_measure():
+    """Rectangular forward / backward on the context-parallel shard shape."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_75_amd as ea
+
+    b, nq, nk, h, d = 1, 8192, 65536, 8, 128
+    off = nk - nq
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(1)
+    mk = lambda n: torch.randn(b, n, h, d, device=dev, generator=g).to(torch.bfloat16)  # noqa: E731
+    q, do, k, v = mk(nq), mk(nq), mk(nk), mk(nk)
+    o, lse = torch.empty_like(q), torch.empty((b, h, nq), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(b, nq, h, h, d), dtype=torch.uint8, device=dev)
+    sc = 1.0 / float(np.sqrt(d))
+    pairs = float(np.minimum(nk, np.maximum(0, np.arange(nq) + off + 1)).sum())
+    fl = 4.0 * d * b * h * pairs
+    t_f = _median_ms(lambda: ea.attn_fwd(q, k, v, o, lse, True, sc, stream, causal_offset=off), stream)
+    t_b = _median_ms(lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, True, sc, stream,
+                                         causal_offset=off), stream)
+    del q, do, k, v, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    out = {"workload": f"last of 8 causal shards of a 65536-token sequence: B={b} Nq={nq} Nk={nk} H={h} d={d} "
+                       f"bf16, causal offset {off}",
+           "unit": "TFLOP/s (allowed query-key pairs)",
+           "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
+           "fwd_tflops": round(fl / (t_f / 1e3) / 1e12, 1),
+           "bwd_tflops": round(2.5 * fl / (t_b / 1e3) / 1e12, 1)}
+    # split-KV on a short-query shape (one 128-row block per head)
+    b, nq, nk, h, splits = 1, 128, 65536, 32, 16
+    q, k, v = mk_shape(g, dev, b, nq, h, d), mk_shape(g, dev, b, nk, h, d), mk_shape(g, dev, b, nk, h, d)
+    o, lse = torch.empty_like(q), torch.empty((b, h, nq), dtype=torch.float32, device=dev)
+    ws = torch.empty(ea.attn_fwd_splitkv_workspace_bytes(b, nq, h, d, splits), dtype=torch.uint8, device=dev)
+    fl = 4.0 * d * b * h * nq * nk
+    t_1 = _median_ms(lambda: ea.attn_fwd(q, k, v, o, lse, False, sc, stream), stream)
+    t_s = _median_ms(lambda: ea.attn_fwd_splitkv(q, k, v, o, lse, ws, False, sc, splits, stream), stream)
+    out["splitkv"] = {"workload": f"B={b} Nq={nq} Nk={nk} H={h} d={d} bf16, non-causal, {splits} splits",
+                      "fwd_ms": round(t_s, 4), "fwd_tflops": round(fl / (t_s / 1e3) / 1e12, 1),
+                      "unsplit_fwd_ms": round(t_1, 4), "speedup": round(t_1 / t_s, 2)}
+    del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def mk_shape(g, dev, b, n, h, d):
+    import torch
+
+    return torch.randn(b, n, h, d, device=dev, generator=g).to(torch.bfloat16)
 
 
 COPY_BYTES = 512 << 20  # calibration copy: reads and writes this many bytes per launch
@@ -472,7 +534,7 @@ def main():
                     help="CPU oracle baseline budget in seconds (0 disables it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sparse", dest="sparse", action="store_false",
-                    help="skip the block-sparse measurement")
+                    help="skip the block-sparse and shard measurements")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain copy of known size first (for counter calibration)")
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "EVIDENCE_DIR"),

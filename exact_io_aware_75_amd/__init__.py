@@ -2,8 +2,10 @@
 
 The compute lives in ``libattn.so`` (hand-written HIP kernels behind a C ABI,
 declared in ``include/attn.h``).  This package is the thin Python binding:
-``attn_fwd`` / ``attn_bwd`` marshal torch device tensors into that ABI, and
-``forward`` / ``backward`` are conveniences that allocate the outputs.  The
+``attn_fwd`` / ``attn_bwd`` / ``attn_fwd_splitkv`` marshal torch device
+tensors into that ABI (block-sparse and rectangular calls through their
+``block_mask`` / ``causal_offset`` arguments), and ``forward`` /
+``backward`` are conveniences that allocate the outputs.  The
 library is loaded on first use; if it is missing every call raises.
 """
 
@@ -12,6 +14,8 @@ from ._lib import (  # noqa: F401
     attn_fwd,
     attn_bwd,
     attn_bwd_workspace_bytes,
+    attn_fwd_splitkv,
+    attn_fwd_splitkv_workspace_bytes,
     forward,
     backward,
     library_path,

@@ -22,7 +22,7 @@ ATTN_DTYPE_BF16 = 1
 # Entry points declared in include/attn.h (checked by the ABI test).
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
            "attn_bwd_workspace_bytes", "attn_fwd_blocksparse", "attn_bwd_blocksparse",
-           "attn_fwd_rect", "attn_bwd_rect",
+           "attn_fwd_rect", "attn_bwd_rect", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
            "attn_strerror", "attn_last_hip_error", "attn_version")
 SPARSE_BLOCK = 128  # ATTN_SPARSE_BLOCK: rows / keys per block of the block mask
 BWD_STAGES = ("attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq")
@@ -67,6 +67,10 @@ def load_library():
     lib.attn_fwd_rect.restype = i
     lib.attn_bwd_rect.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, ll, f, vp]
     lib.attn_bwd_rect.restype = i
+    lib.attn_fwd_splitkv.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, i, ll, f, i, vp]
+    lib.attn_fwd_splitkv.restype = i
+    lib.attn_fwd_splitkv_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_fwd_splitkv_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_strerror.argtypes = [i]
@@ -183,6 +187,35 @@ def attn_fwd(q, k, v, o, lse, causal: bool, scale: float, stream=None, block_mas
         raise AttnError(st, name)
 
 
+def attn_fwd_splitkv_workspace_bytes(b: int, nq: int, hq: int, d: int, num_splits: int) -> int:
+    return int(load_library().attn_fwd_splitkv_workspace_bytes(b, nq, hq, d, num_splits))
+
+
+def attn_fwd_splitkv(q, k, v, o, lse, workspace, causal: bool, scale: float, num_splits: int,
+                     stream=None, causal_offset=None) -> None:
+    """Enqueue the split-KV forward pass (keys cut into ``num_splits`` runs
+    processed in parallel, then merged); ``workspace`` is a uint8 device
+    tensor of at least ``attn_fwd_splitkv_workspace_bytes`` bytes."""
+    import torch
+
+    lib = load_library()
+    b, n, hq, hkv, d = _dims(q, k)
+    nk = k.shape[1]
+    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, nk, hkv, d), "k"),
+                       (v, (b, nk, hkv, d), "v"), (o, (b, n, hq, d), "o")):
+        _check(t, shp, q.dtype, q.device, nm)
+    _check(lse, (b, hq, n), torch.float32, q.device, "lse")
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    off = (nk - n) if causal_offset is None else int(causal_offset)
+    st = lib.attn_fwd_splitkv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), b, n, nk, hq, hkv, d,
+                              _dtype_code(q), int(bool(causal)), off, float(scale), int(num_splits),
+                              _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_splitkv")
+
+
 def attn_bwd_workspace_bytes(b: int, n: int, hq: int, hkv: int, d: int) -> int:
     return int(load_library().attn_bwd_workspace_bytes(b, n, hq, hkv, d))
 
@@ -242,15 +275,25 @@ def _default_scale(d: int, scale):
     return 1.0 / math.sqrt(d) if scale is None else float(scale)
 
 
-def forward(q, k, v, causal: bool = False, scale=None, stream=None, block_mask=None, causal_offset=None):
+def forward(q, k, v, causal: bool = False, scale=None, stream=None, block_mask=None, causal_offset=None,
+            num_splits=None):
     """Allocate ``o`` and ``lse`` and run ``attn_fwd`` (with a block mask
     ``attn_fwd_blocksparse``; with Nk != Nq or a causal offset
-    ``attn_fwd_rect``); returns (o, lse)."""
+    ``attn_fwd_rect``; with ``num_splits`` ``attn_fwd_splitkv``, allocating
+    its workspace); returns (o, lse)."""
     import torch
 
     b, n, hq, _, d = _dims(q, k)
     o = torch.empty_like(q)
     lse = torch.empty((b, hq, n), dtype=torch.float32, device=q.device)
+    if num_splits is not None:
+        if block_mask is not None:
+            raise ValueError("split-KV and block-sparse attention do not combine")
+        ws = torch.empty(attn_fwd_splitkv_workspace_bytes(b, n, hq, d, num_splits), dtype=torch.uint8,
+                         device=q.device)
+        attn_fwd_splitkv(q, k, v, o, lse, ws, causal, _default_scale(d, scale), num_splits, stream,
+                         causal_offset=causal_offset)
+        return o, lse
     attn_fwd(q, k, v, o, lse, causal, _default_scale(d, scale), stream, block_mask=block_mask,
              causal_offset=causal_offset)
     return o, lse

@@ -97,7 +97,7 @@ int clamp_offset(long long off, int Nq, int Nk) {
 int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
                const unsigned char* block_mask, int mask_heads, int B, int N, int Nk, int Hq,
                int Hkv, int d, int dtype, int causal, long long causal_offset, float scale,
-               void* stream) {
+               void* stream, int splits = 1, void* workspace = nullptr, size_t workspace_bytes = 0) {
   if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULLPTR;
   int st = check_shape(B, N, Hq, Hkv, d);
   if (st != ATTN_OK) return st;
@@ -131,6 +131,18 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   a.sp = sp;
   a.Nk = Nk;
   a.coff = clamp_offset(causal_offset, N, Nk);
+  a.splits = 1;
+  a.split_len = 0;
+  a.opart = nullptr;
+  a.lsepart = nullptr;
+  if (workspace) {  // split-KV: keys in `splits` runs of a multiple of 128
+    const attn::SplitWorkspace w = attn::split_workspace_layout(B, N, Hq, d, splits);
+    const int per = (Nk + splits - 1) / splits;
+    a.splits = splits;
+    a.split_len = (per + 127) / 128 * 128;
+    a.opart = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.opart_off);
+    a.lsepart = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.lsepart_off);
+  }
   hipError_t e = attn::launch_fwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {
@@ -154,6 +166,30 @@ int attn_fwd_rect(const void* q, const void* k, const void* v, void* o, float* l
                   float scale, void* stream) {
   return fwd_common(q, k, v, o, lse, nullptr, 0, B, Nq, Nk, Hq, Hkv, d, dtype, causal, causal_offset,
                     scale, stream);
+}
+
+size_t attn_fwd_splitkv_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits) {
+  if (B < 1 || Nq < 1 || Hq < 1 || (d != 64 && d != 128 && d != 256) || num_splits < 1 ||
+      num_splits > ATTN_MAX_SPLITS)
+    return 0;
+  return attn::split_workspace_layout(B, Nq, Hq, d, num_splits).total;
+}
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                     size_t workspace_bytes, int B, int Nq, int Nk, int Hq, int Hkv, int d, int dtype,
+                     int causal, long long causal_offset, float scale, int num_splits, void* stream) {
+  if (num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return ATTN_ERR_SHAPE;
+  const size_t need = attn_fwd_splitkv_workspace_bytes(B, Nq, Hq, d, num_splits);
+  if (!workspace || need == 0 || workspace_bytes < need) {
+    // shape errors take precedence over a workspace error
+    if (!q || !k || !v || !o || !lse) return ATTN_ERR_NULLPTR;
+    int st = check_shape(B, Nq, Hq, Hkv, d);
+    if (st == ATTN_OK) st = check_shape(B, Nk, Hq, Hkv, d);
+    return st != ATTN_OK ? st : ATTN_ERR_WORKSPACE;
+  }
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  return fwd_common(q, k, v, o, lse, nullptr, 0, B, Nq, Nk, Hq, Hkv, d, dtype, causal, causal_offset,
+                    scale, stream, num_splits, workspace, workspace_bytes);
 }
 
 int attn_fwd_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -63,9 +63,11 @@ namespace {
 // staged once per 256 query rows.  Causal: four, since the wavefronts of a
 // diagonal block have unequal trip counts and wait for the longest at every
 // barrier.  d = 256: four (one wavefront per SIMD).  Block-sparse: four, so
-// that a workgroup's 128 rows are one row of the block mask.
-template <int D, bool CAUSAL, bool SPARSE = false> struct FwdWG {
-  static constexpr int WAVES = (D <= 128 && !CAUSAL && !SPARSE) ? 8 : 4;
+// that a workgroup's 128 rows are one row of the block mask.  Split-KV: four,
+// since it serves short query sequences, where 256-row blocks would be
+// mostly past the end.
+template <int D, bool CAUSAL, bool SPARSE = false, bool SPLIT = false> struct FwdWG {
+  static constexpr int WAVES = (D <= 128 && !CAUSAL && !SPARSE && !SPLIT) ? 8 : 4;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BM = WAVES * 32;
 };
@@ -92,9 +94,9 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Wavefronts per SIMD the register budget is cut for: two for d <= 128; at
 // d = 256 the resident Q (64 registers) and O^T (128) leave too little for two.
-template <int D, bool CAUSAL, bool SPARSE> struct FwdOcc {
+template <int D, bool CAUSAL, bool SPARSE, bool SPLIT> struct FwdOcc {
   static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1;
-  static constexpr int MIN_WG_PER_CU = WAVES_PER_SIMD * 4 / FwdWG<D, CAUSAL, SPARSE>::WAVES;  // launch-bounds form
+  static constexpr int MIN_WG_PER_CU = WAVES_PER_SIMD * 4 / FwdWG<D, CAUSAL, SPARSE, SPLIT>::WAVES;  // launch-bounds form
 };
 
 template <int I, int N, typename F>
@@ -113,20 +115,22 @@ template <int D> struct FwdPrefetch {
   static constexpr int V = 2;
 };
 
-template <typename Tag, int D, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__((FwdWG<D, CAUSAL, SPARSE>::THREADS), (FwdOcc<D, CAUSAL, SPARSE>::MIN_WG_PER_CU))
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT>
+__global__ void __launch_bounds__((FwdWG<D, CAUSAL, SPARSE, SPLIT>::THREADS),
+                                  (FwdOcc<D, CAUSAL, SPARSE, SPLIT>::MIN_WG_PER_CU))
 attn_fwd_kernel(FwdArgs a) {
   constexpr int BN = FwdTile<D>::BN;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILE = BN * D;          // elements per K or V tile (8192)
-  constexpr int FWD_WAVES = FwdWG<D, CAUSAL, SPARSE>::WAVES;
-  constexpr int FWD_BM = FwdWG<D, CAUSAL, SPARSE>::BM;
-  constexpr int LPT = TILE / 8 / FwdWG<D, CAUSAL, SPARSE>::THREADS;  // 16-byte loads per thread per tensor
+  using WG = FwdWG<D, CAUSAL, SPARSE, SPLIT>;
+  constexpr int FWD_WAVES = WG::WAVES;
+  constexpr int FWD_BM = WG::BM;
+  constexpr int LPT = TILE / 8 / WG::THREADS;  // 16-byte loads per thread per tensor
   constexpr int NKK = D / 16;           // MFMA k-steps over d
   constexpr int NSB = BN / 32;          // 32-key sub-blocks per tile
   constexpr int NDB = D / 32;           // 32-wide d blocks of O
   constexpr int NKS = BN / 16;          // k-steps over keys in P V
-  static_assert(TILE == 8192 && LPT * 8 * FwdWG<D, CAUSAL, SPARSE>::THREADS == TILE, "tile shape");
+  static_assert(TILE == 8192 && LPT * 8 * WG::THREADS == TILE, "tile shape");
   constexpr int TPB = SPARSE_BLOCK / BN;  // key tiles per block of the mask
   static_assert(!SPARSE || FWD_BM == SPARSE_BLOCK, "one workgroup per row of the block mask");
 
@@ -160,15 +164,31 @@ attn_fwd_kernel(FwdArgs a) {
   const size_t q_row = (size_t)a.Hq * D;   // elements between consecutive query rows
   const size_t kv_row = (size_t)a.Hkv * D;
   const uint16_t* qbase = (const uint16_t*)a.q + ((size_t)b * a.N * a.Hq + h) * D;
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.Nk * a.Hkv + g) * D;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.Nk * a.Hkv + g) * D;
+  // Split-KV: this workgroup's keys are [key_base, key_base + nk) of the
+  // sequence; seen from them, the causal offset moves by -key_base.
+  const int key_base = SPLIT ? (int)blockIdx.y * a.split_len : 0;
+  const int nk = SPLIT ? max(0, min(a.split_len, a.Nk - key_base)) : a.Nk;
+  const int coff = a.coff - key_base;
+  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)key_base * kv_row;
+  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)key_base * kv_row;
 
   const int row0 = rb * FWD_BM;                 // first query row of the workgroup
   const int wrow0 = row0 + wave * 32;           // first query row of this wavefront
   const int qrow = wrow0 + l32;                 // this lane's query row
   const bool qvalid = qrow < a.N;
+  // split-KV partials of this row
+  float* const opart = SPLIT ? a.opart + ((((size_t)blockIdx.y * a.B + b) * a.N + qrow) * a.Hq + h) * D : nullptr;
+  float* const lsepart = SPLIT ? a.lsepart + (((size_t)blockIdx.y * a.B + b) * a.Hq + h) * a.N + qrow : nullptr;
   // O = 0 and LSE = -inf for the rows of a workgroup that sees no key at all
   auto write_empty = [&]() __attribute__((always_inline)) {
+    if (SPLIT) {
+      if (qvalid) {
+#pragma unroll
+        for (int i = 0; i < D / 8; ++i) *(f32x4_t*)(opart + 8 * i + 4 * half) = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+        if (half == 0) *lsepart = -INFINITY;
+      }
+      return;
+    }
     if (qvalid) {
       uint16_t* orow = (uint16_t*)a.o + ((size_t)b * a.N * a.Hq + h) * D + (size_t)qrow * q_row;
 #pragma unroll
@@ -216,18 +236,18 @@ attn_fwd_kernel(FwdArgs a) {
 
   // ---- key tiles: the workgroup's trip count and this wavefront's share ----
   // (causal: query i sees keys j <= i + coff)
-  const int ntiles_all = (a.Nk + BN - 1) / BN;
+  const int ntiles_all = (nk + BN - 1) / BN;
   int ntiles = ntiles_all;   // tiles the workgroup streams through LDS
   int nwave = ntiles_all;    // tiles this wavefront computes
-  int nfull = a.Nk / BN;     // leading tiles that need no element mask
+  int nfull = nk / BN;       // leading tiles that need no element mask
   if (CAUSAL) {
-    ntiles = max(0, min(ntiles_all, floor_div(min(row0 + FWD_BM, a.N) - 1 + a.coff, BN) + 1));
-    nwave = max(0, min(ntiles, floor_div(wrow0 + 31 + a.coff, BN) + 1));
-    nfull = max(0, min(min(nfull, ntiles), floor_div(wrow0 + 1 + a.coff, BN)));
-    if (ntiles == 0) {  // an offset can leave every row of the block without a key
-      write_empty();
-      return;
-    }
+    ntiles = max(0, min(ntiles_all, floor_div(min(row0 + FWD_BM, a.N) - 1 + coff, BN) + 1));
+    nwave = max(0, min(ntiles, floor_div(wrow0 + 31 + coff, BN) + 1));
+    nfull = max(0, min(min(nfull, ntiles), floor_div(wrow0 + 1 + coff, BN)));
+  }
+  if ((CAUSAL || SPLIT) && ntiles == 0) {  // an offset or an empty split: no key for any row
+    write_empty();
+    return;
   }
   if constexpr (SPARSE) {
     // The counts above are bounds on the key tile index.  Every listed block
@@ -262,7 +282,7 @@ attn_fwd_kernel(FwdArgs a) {
     const uint16_t* src = base + (size_t)j * BN * kv_row;
     // bytes from the tile's first row to the sequence end: < 2^32, as the host
     // bounds N * H * d below 2^31 elements
-    const uint32_t nrec = (uint32_t)(a.Nk - j * BN) * (uint32_t)kv_row * 2u;
+    const uint32_t nrec = (uint32_t)(nk - j * BN) * (uint32_t)kv_row * 2u;
     const __amdgpu_buffer_rsrc_t rs =
         __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)nrec, 0x00020000);
 #pragma unroll
@@ -389,7 +409,7 @@ attn_fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = key0 + 32 * sb + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool ok = key < a.Nk && (!CAUSAL || key <= qrow + a.coff);
+        const bool ok = key < nk && (!CAUSAL || key <= qrow + coff);
         s[sb][r] = ok ? s[sb][r] : -INFINITY;
       }
   };
@@ -529,7 +549,23 @@ attn_fwd_kernel(FwdArgs a) {
   }
   // A row with no allowed key (causal, qrow + coff < 0; its accumulators
   // are not meaningful) gets O = 0 and LSE = -inf; the test is on integers.
-  const bool empty = CAUSAL && qrow + a.coff < 0;
+  const bool empty = CAUSAL && qrow + coff < 0;
+  if (SPLIT) {  // fp32 partials, each normalised by its own sum
+    if (qvalid) {
+      const float inv = 1.0f / ltot;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4_t w = {oacc[db][4 * q4] * inv, oacc[db][4 * q4 + 1] * inv, oacc[db][4 * q4 + 2] * inv,
+                       oacc[db][4 * q4 + 3] * inv};
+          if (empty) w = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+          *(f32x4_t*)(opart + 32 * db + 8 * q4 + 4 * half) = w;
+        }
+      if (half == 0) *lsepart = empty ? -INFINITY : (m_ref + log2f(ltot)) * 0.69314718055994530942f;
+    }
+    return;
+  }
   if (qvalid) {
     const float inv = 1.0f / ltot;
     uint16_t* orow = (uint16_t*)a.o + ((size_t)b * a.N * a.Hq + h) * D + (size_t)qrow * q_row;
@@ -550,24 +586,86 @@ attn_fwd_kernel(FwdArgs a) {
   }
 }
 
+// Split-KV merge: for each query row, LSE = ln sum_s exp(LSE_s) and
+// O = sum_s exp(LSE_s - LSE) O_s over the splits' fp32 partials (the exact
+// combination of softmax over disjoint key sets); rows no split saw get
+// O = 0, LSE = -inf.  One thread per 8 elements of a row; HBM-bound.
+template <typename Tag, int D>
+__global__ void __launch_bounds__(256) attn_fwd_merge_kernel(FwdArgs a) {
+  constexpr int CPR = D / 8;       // 8-element chunks per row
+  constexpr int ROWS = 256 / CPR;  // rows per workgroup
+  const int tid = threadIdx.x;
+  const int rloc = tid / CPR;
+  const int c = tid - rloc * CPR;
+  const long long row = (long long)blockIdx.x * ROWS + rloc;  // (b * N + n) * Hq + h
+  const long long nrows = (long long)a.B * a.N * a.Hq;
+  if (row >= nrows) return;
+  const long long bn = row / a.Hq;
+  const int h = (int)(row - bn * a.Hq);
+  const long long b = bn / a.N;
+  const int n = (int)(bn - b * a.N);
+  const size_t lstride = (size_t)a.B * a.Hq * a.N;          // between the splits' LSE arrays
+  const float* lp = a.lsepart + ((size_t)b * a.Hq + h) * a.N + n;
+  float m = -INFINITY;
+  for (int s = 0; s < a.splits; ++s) m = fmaxf(m, lp[s * lstride]);
+  f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  const bool any = m > -INFINITY;
+  if (any) {
+    const float* op = a.opart + (size_t)row * D + 8 * c;
+    for (int s = 0; s < a.splits; ++s) {
+      const float w = fast_exp2((lp[s * lstride] - m) * 1.4426950408889634f);  // 0 for an empty split
+      const f32x4_t* src = (const f32x4_t*)(op + (size_t)s * nrows * D);
+      acc0 += w * src[0];
+      acc1 += w * src[1];
+      wsum += w;
+    }
+  }
+  const float inv = any ? 1.0f / wsum : 0.f;
+  const u32x4_t out = {pack2(Tag{}, acc0[0] * inv, acc0[1] * inv), pack2(Tag{}, acc0[2] * inv, acc0[3] * inv),
+                       pack2(Tag{}, acc1[0] * inv, acc1[1] * inv), pack2(Tag{}, acc1[2] * inv, acc1[3] * inv)};
+  *(u32x4_t*)((uint16_t*)a.o + (size_t)row * D + 8 * c) = out;
+  if (c == 0) a.lse[((size_t)b * a.Hq + h) * a.N + n] = any ? m + logf(wsum) : -INFINITY;
+}
+
 }  // namespace
 
-template <typename Tag, int D, bool CAUSAL, bool SPARSE>
+SplitWorkspace split_workspace_layout(int B, int N, int Hq, int d, int splits) {
+  auto align256 = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  SplitWorkspace w;
+  w.opart_off = 0;
+  w.lsepart_off = align256((size_t)splits * B * N * Hq * d * sizeof(float));
+  w.total = w.lsepart_off + align256((size_t)splits * B * Hq * N * sizeof(float));
+  return w;
+}
+
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT>
 hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t stream) {
-  using WG = FwdWG<D, CAUSAL, SPARSE>;
+  using WG = FwdWG<D, CAUSAL, SPARSE, SPLIT>;
   const int nblk = (a.N + WG::BM - 1) / WG::BM;
   const long long total = (long long)nblk * a.Hq * a.B;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (SPARSE && (a.sp.bmask == nullptr || a.sp.nb != nblk || a.sp.nb > SPARSE_MAX_NB || a.Nk != a.N || a.coff != 0))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)total), dim3(WG::THREADS), 0,
-                     stream, a);
+  if (SPLIT && (a.splits < 1 || a.splits > 65535 || a.split_len < 1 || a.split_len % SPARSE_BLOCK != 0 ||
+                a.opart == nullptr || a.lsepart == nullptr))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, SPARSE, SPLIT>), dim3((unsigned)total, SPLIT ? a.splits : 1),
+                     dim3(WG::THREADS), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (!SPLIT || e != hipSuccess) return e;
+  constexpr int ROWS = 256 / (D / 8);
+  const long long grid = ((long long)a.B * a.N * a.Hq + ROWS - 1) / ROWS;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((attn_fwd_merge_kernel<Tag, D>), dim3((unsigned)grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <typename Tag, int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  return a.sp.bmask ? launch_fwd_s<Tag, D, CAUSAL, true>(a, stream) : launch_fwd_s<Tag, D, CAUSAL, false>(a, stream);
+  if (a.sp.bmask) return launch_fwd_s<Tag, D, CAUSAL, true, false>(a, stream);
+  if (a.splits > 1 || a.opart) return launch_fwd_s<Tag, D, CAUSAL, false, true>(a, stream);
+  return launch_fwd_s<Tag, D, CAUSAL, false, false>(a, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream) {

@@ -30,6 +30,12 @@ struct FwdArgs {
   int B, N, Hq, Hkv;
   int Nk;            // keys (K/V rows per sequence); N is the number of queries
   int coff;          // causal: query i sees key j iff j <= i + coff (clamped to [-N, Nk])
+  // split-KV: workgroup (x, y) covers keys [y split_len, (y + 1) split_len)
+  // and writes fp32 partials that a merge kernel combines into o and lse
+  int splits;        // 1: no split
+  int split_len;     // keys per split, a multiple of 128
+  float* opart;      // [splits, B, N, Hq, d] fp32: each split's O, normalised by its own sum
+  float* lsepart;    // [splits, B, Hq, N] fp32: each split's natural-log LSE (-inf: no key)
   int group;         // Hq / Hkv
   int neg_scale;     // 1 if scale < 0 (folded into Q's sign)
   float scale_log2;  // |scale| * log2(e)
@@ -64,6 +70,11 @@ struct BwdWorkspace {
 BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int Hkv, int d);
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream);
+// Split-KV layout of the forward workspace (offsets in bytes, 256-byte aligned).
+struct SplitWorkspace {
+  size_t opart_off, lsepart_off, total;
+};
+SplitWorkspace split_workspace_layout(int B, int N, int Hq, int d, int splits);
 // stage_mask: bit 0 = D preprocess, bit 1 = dK/dV kernel, bit 2 = dQ kernel
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, int d, bool causal, int stage_mask,
                       hipStream_t stream);

@@ -163,6 +163,32 @@ int attn_bwd_rect(const void* q, const void* k, const void* v, const void* o, co
                   int dtype, int causal, long long causal_offset, float scale, void* stream);
 
 /*
+ * Split-KV forward: attn_fwd_rect with the keys cut into `num_splits` runs
+ * (each a multiple of 128 keys, ceil(Nk / num_splits) rounded up; trailing
+ * runs may be empty) that separate workgroups process in parallel, then
+ * merged exactly, LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s,
+ * from fp32 partials in `workspace`.  For shapes with few query rows per
+ * (batch, head) -- short Nq, small B * Hq -- where one workgroup per 128 or
+ * 256 query rows leaves most of the GPU idle (the pages parallelise over the
+ * sequence for this reason: FlashAttention-2 announcement, section "具体实现").
+ * Arguments as attn_fwd_rect, plus:
+ *   num_splits       1 .. ATTN_MAX_SPLITS
+ *   workspace        device memory, 16-byte aligned, at least
+ *                    attn_fwd_splitkv_workspace_bytes(B, Nq, Hq, d,
+ *                    num_splits) bytes (fp32 partial O and LSE of every
+ *                    split); contents on entry ignored, on exit undefined
+ * Calls sharing a workspace must be ordered on one stream.
+ */
+#define ATTN_MAX_SPLITS 256
+
+size_t attn_fwd_splitkv_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits);
+
+int attn_fwd_splitkv(const void* q, const void* k, const void* v, void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, int B, int Nq, int Nk, int Hq,
+                     int Hkv, int d, int dtype, int causal, long long causal_offset, float scale,
+                     int num_splits, void* stream);
+
+/*
  * Block-sparse attention.  The FlashAttention-1 news page benchmarks a
  * block-sparse variant of the method beside the dense one (its paragraph on
  * runtime and memory against the A100 baselines); the pages do not define

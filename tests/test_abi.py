@@ -173,3 +173,19 @@ def test_rect_rejects_invalid_arguments(lib):
         A, A, A, A, A, A, A, A, A, A, ws_bytes, 1, 128, Nk, 2, 2, 64, 1, 1, -(1 << 40), 0.125, None)
     assert bwd(ws_bytes=ws - 1) == c["ATTN_ERR_WORKSPACE"]
     assert bwd(Nk=-1) == c["ATTN_ERR_SHAPE"]
+
+
+def test_splitkv_rejects_invalid_arguments(lib):
+    c = _status_codes()
+    need = lib.attn_fwd_splitkv_workspace_bytes(1, 128, 2, 64, 4)
+    assert need >= 4 * 128 * 2 * 64 * 4
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 128, 2, 64, 0) == 0
+    assert lib.attn_fwd_splitkv_workspace_bytes(1, 128, 2, 64, 257) == 0
+    f = lambda splits=4, ws=A, ws_bytes=need, q=A: lib.attn_fwd_splitkv(  # noqa: E731
+        q, A, A, A, A, ws, ws_bytes, 1, 128, 1000, 2, 2, 64, 1, 0, 0, 0.125, splits, None)
+    assert f(splits=0) == c["ATTN_ERR_SHAPE"]
+    assert f(splits=1000) == c["ATTN_ERR_SHAPE"]
+    assert f(ws=None) == c["ATTN_ERR_WORKSPACE"]
+    assert f(ws_bytes=need - 1) == c["ATTN_ERR_WORKSPACE"]
+    assert f(ws=A + 4) == c["ATTN_ERR_ALIGN"]
+    assert f(q=None) == c["ATTN_ERR_NULLPTR"]

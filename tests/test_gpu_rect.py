@@ -137,3 +137,39 @@ def test_full_size_shard(gpu_device):
     log(f"  head {hh}: max|ddK|={max_err(dk[0, :, hh], rdk)[0]:.3e} max|ddV|={max_err(dv[0, :, hh], rdv)[0]:.3e}")
     assert excess(dk[0, :, hh], rdk, TOL_GRAD, "bf16") <= 0
     assert excess(dv[0, :, hh], rdv, TOL_GRAD, "bf16") <= 0
+
+
+SPLIT = [
+    # b, nq, nk, hq, hkv, d, dtype, causal, offset, splits
+    (1, 1, 5000, 4, 1, 128, "bf16", False, None, 8),
+    (2, 17, 3000, 2, 2, 64, "bf16", True, None, 5),
+    (1, 128, 8192, 8, 2, 128, "fp16", True, None, 16),
+    (1, 300, 1000, 2, 2, 256, "bf16", True, -100, 3),
+    (1, 64, 700, 2, 1, 128, "bf16", False, None, 40),   # more splits than 128-key runs: empty splits
+    (1, 100, 100, 2, 2, 64, "bf16", True, None, 1),
+]
+
+
+@pytest.mark.parametrize("b,nq,nk,hq,hkv,d,dtype,causal,offset,splits", SPLIT)
+def test_splitkv_matches_oracle(gpu_device, b, nq, nk, hq, hkv, d, dtype, causal, offset, splits):
+    import torch
+    import exact_io_aware_75_amd as ea
+
+    x = make_rect_inputs(b, nq, nk, hq, hkv, d, dtype, cfg_id=45, seed=nq + splits)
+    scale = 1.0 / np.sqrt(d)
+    tag = f"split-KV b{b} nq{nq} nk{nk} hq{hq} hkv{hkv} d{d} {dtype} causal={causal} offset={offset} splits={splits}"
+    log(tag)
+    q, k, v = (gen.to_torch(x[t], dtype, gpu_device) for t in ("q", "k", "v"))
+    o, lse = ea.forward(q, k, v, causal=causal, scale=scale, causal_offset=offset, num_splits=splits)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy().astype(np.float64)
+    lse = lse.cpu().numpy().astype(np.float64)
+    ro, rlse = oracle.attention_fwd(x["q"], x["k"], x["v"], causal, scale, causal_offset=offset)
+    fin = np.isfinite(rlse)
+    log(f"  o err {max_err(o, ro)[0]:.2e}  lse err {np.abs(lse[fin] - rlse[fin]).max() if fin.any() else 0:.2e}"
+        f"  empty rows {int((~fin).sum())}")
+    assert np.isfinite(o).all()
+    assert excess(o, ro, TOL_O, dtype) <= 0
+    assert np.array_equal(np.isfinite(lse), fin)
+    if fin.any():
+        assert np.abs(lse[fin] - rlse[fin]).max() <= TOL_LSE
