@@ -524,6 +524,40 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
     print("\n".join(lines))
 
 
+def summarize_trace(trace_dir, out_name, title, cmd, name_filter=""):
+    """Write profiles/<out_name>: calls and durations per kernel and grid shape
+    of a rocprofv3 --kernel-trace run (its kernel_trace.csv), for the kernels
+    whose name holds `name_filter` and "attn_"."""
+    import glob
+
+    hits = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not hits:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    durs = {}  # (kernel, grid in workgroups) -> durations
+    for r in _read_csv(hits[0]):
+        nm = r["Kernel_Name"]
+        if "attn_" not in nm or name_filter not in nm:
+            continue
+        wg = [int(r[f"Grid_Size_{a}"]) // max(1, int(r[f"Workgroup_Size_{a}"])) for a in "XYZ"]
+        key = (nm, "x".join(str(v_) for v_ in wg))
+        durs.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def short(nm):
+        nm = nm.replace("(anonymous namespace)::", "").replace("attn::", "")
+        return nm[nm.find("attn_"):nm.find("(")] if "attn_" in nm else nm[:60]
+
+    lines = [title, "", f"trace: {cmd}", "",
+             f"{'kernel':52s} {'grid (WGs)':>12s} {'calls':>5s} {'avg_us':>9s} {'median_us':>9s} "
+             f"{'min_us':>9s} {'max_us':>9s}"]
+    for (nm, grid), ds in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        s = sorted(ds)
+        lines.append(f"{short(nm)[:52]:52s} {grid:>12s} {len(s):5d} {sum(s) / len(s):9.2f} "
+                     f"{s[len(s) // 2]:9.2f} {s[0]:9.2f} {s[-1]:9.2f}")
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -540,9 +574,15 @@ def main():
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "EVIDENCE_DIR"),
                     help="write profiles/ summaries from rocprofv3 CSV output and exit")
     ap.add_argument("--summarize-cmds", default="{}", help="JSON dict of the commands that made them")
+    ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT_NAME", "TITLE", "CMD"),
+                    help="write a per-kernel duration table of a kernel-trace run to profiles/OUT_NAME and exit")
+    ap.add_argument("--trace-filter", default="", help="only kernels whose name contains this")
     args = ap.parse_args()
     if args.summarize:
         summarize_profiles(*args.summarize, json.loads(args.summarize_cmds))
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, name_filter=args.trace_filter)
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
