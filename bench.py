@@ -29,7 +29,11 @@ Prints one JSON line.  Besides the throughput it carries
                 d = 128 (FLOPs over the allowed query-key pairs); and the
                 split-KV forward (attn_fwd_splitkv) on a short-query shape,
                 128 queries against 65536 keys, B = 1, H = 32, d = 128,
-                against the unsplit kernel.
+                against the unsplit kernel;
+  standard      standard attention (attn_fwd_standard / attn_bwd_standard),
+                which writes the N x N scores and probabilities to HBM, against
+                the tiled kernels on the step's shape: times, speed-ups, extra
+                device memory and algorithmic HBM bytes of each.
 --sweep also prints per-workload forward/backward TFLOP/s for every full-size
 configuration to stderr.
 """
@@ -223,6 +227,8 @@ def run(args):
     if args.sparse:
         line["blocksparse"] = blocksparse_measure()
         line["shard"] = shard_measure()
+    if args.standard:
+        line["standard"] = standard_measure()
     if args.sweep:
         sweep()
     if args.cpu_seconds > 0:
@@ -392,6 +398,56 @@ def shard_measure():
                       "fwd_ms": round(t_s, 4), "fwd_tflops": round(fl / (t_s / 1e3) / 1e12, 1),
                       "unsplit_fwd_ms": round(t_1, 4), "speedup": round(t_1 / t_s, 2)}
     del q, k, v, o, lse, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def standard_measure():
+    """Standard (materialising) attention against the tiled kernels on the
+    benchmark workload: time (HIP events, median of 10), device memory beyond
+    the inputs and outputs, and the algorithmic HBM bytes of each."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_75_amd as ea
+
+    w = WORKLOAD
+    b, n, h, d = w["b"], w["n"], w["h"], w["d"]
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(2)
+    q, k, v, do = (mk_shape(g, dev, b, n, h, d) for _ in range(4))
+    o, lse = torch.empty_like(q), torch.empty((b, h, n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    std_ws = ea.attn_standard_workspace_bytes(b, n, h, h, d)
+    ws_s = torch.empty(std_ws, dtype=torch.uint8, device=dev)
+    ws_t = torch.empty(ea.attn_bwd_workspace_bytes(b, n, h, h, d), dtype=torch.uint8, device=dev)
+    sc = 1.0 / float(np.sqrt(d))
+    bh, nd, nn = b * h, n * d, n * n
+    out = {"workload": f"B={b} N={n} H={h} d={d} bf16 (the step's shape)",
+           "what": "standard attention: S = scale QK^T (fp32) and P = softmax(S) written to HBM in full, "
+                   "O = PV; backward reads the stored P (dV = P^T dO, dP = dO V^T, dS, dQ, dK)",
+           "extra_memory_bytes": {"standard": std_ws, "tiled": int(ws_t.numel()) + 4 * bh * n,
+                                  "ratio": round(std_ws / (ws_t.numel() + 4 * bh * n), 1)},
+           # S write + read, P write + read (fwd); P read twice, dP write + read, dS write + 2 reads (bwd)
+           "algorithmic_hbm_bytes": {"standard_fwd": bh * (12 * nn + 8 * nd + 4 * n),
+                                     "standard_bwd": bh * (18 * nn + 14 * nd),
+                                     "tiled_fwd": bh * (8 * nd + 4 * n), "tiled_bwd": bh * (16 * nd + 8 * n)}}
+    for causal in (False, True):
+        t_sf = _median_ms(lambda: ea.attn_fwd_standard(q, k, v, o, lse, ws_s, causal, sc, stream), stream)
+        t_sb = _median_ms(lambda: ea.attn_bwd_standard(q, k, v, do, dq, dk, dv, ws_s, causal, sc, stream), stream)
+        t_tf = _median_ms(lambda: ea.attn_fwd(q, k, v, o, lse, causal, sc, stream), stream)
+        t_tb = _median_ms(lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws_t, causal, sc, stream), stream)
+        hb = out["algorithmic_hbm_bytes"]
+        out["causal" if causal else "noncausal"] = {
+            "standard_fwd_ms": round(t_sf, 4), "standard_bwd_ms": round(t_sb, 4),
+            "tiled_fwd_ms": round(t_tf, 4), "tiled_bwd_ms": round(t_tb, 4),
+            "speedup_fwd": round(t_sf / t_tf, 2), "speedup_bwd": round(t_sb / t_tb, 2),
+            "speedup_fwd_bwd": round((t_sf + t_sb) / (t_tf + t_tb), 2),
+            "standard_fwd_hbm_GBps": round(hb["standard_fwd"] / (t_sf / 1e3) / 1e9, 1),
+            "standard_bwd_hbm_GBps": round(hb["standard_bwd"] / (t_sb / 1e3) / 1e9, 1)}
+    del q, k, v, do, o, lse, dq, dk, dv, ws_s, ws_t
     torch.cuda.empty_cache()
     return out
 
@@ -569,6 +625,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sparse", dest="sparse", action="store_false",
                     help="skip the block-sparse and shard measurements")
+    ap.add_argument("--no-standard", dest="standard", action="store_false",
+                    help="skip the standard (materialising) attention comparison")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run a plain copy of known size first (for counter calibration)")
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "EVIDENCE_DIR"),

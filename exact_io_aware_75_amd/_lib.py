@@ -23,6 +23,7 @@ ATTN_DTYPE_BF16 = 1
 EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq",
            "attn_bwd_workspace_bytes", "attn_fwd_blocksparse", "attn_bwd_blocksparse",
            "attn_fwd_rect", "attn_bwd_rect", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
+           "attn_fwd_standard", "attn_bwd_standard", "attn_standard_workspace_bytes",
            "attn_strerror", "attn_last_hip_error", "attn_version")
 SPARSE_BLOCK = 128  # ATTN_SPARSE_BLOCK: rows / keys per block of the block mask
 BWD_STAGES = ("attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq")
@@ -73,6 +74,12 @@ def load_library():
     lib.attn_fwd_splitkv_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_fwd_standard.argtypes = [vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
+    lib.attn_fwd_standard.restype = i
+    lib.attn_bwd_standard.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
+    lib.attn_bwd_standard.restype = i
+    lib.attn_standard_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.attn_standard_workspace_bytes.restype = sz
     lib.attn_strerror.argtypes = [i]
     lib.attn_strerror.restype = ctypes.c_char_p
     lib.attn_last_hip_error.argtypes = []
@@ -269,6 +276,61 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: 
                                       _ptr(block_mask), mh, *tail)
     if st != 0:
         raise AttnError(st, stage)
+
+
+def attn_standard_workspace_bytes(b: int, n: int, hq: int, hkv: int, d: int) -> int:
+    return int(load_library().attn_standard_workspace_bytes(b, n, hq, hkv, d))
+
+
+def _check_ws(workspace, device):
+    if workspace.device != device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    return workspace.numel() * workspace.element_size()
+
+
+def attn_fwd_standard(q, k, v, o, lse, workspace, causal: bool, scale: float, stream=None) -> None:
+    """Enqueue standard (materialising) attention's forward pass: S, then P,
+    in full in ``workspace`` (a uint8 device tensor of at least
+    ``attn_standard_workspace_bytes`` bytes), then ``o`` and ``lse``."""
+    import torch
+
+    lib = load_library()
+    b, n, hq, hkv, d = _dims(q, k)
+    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, n, hkv, d), "k"), (v, (b, n, hkv, d), "v"),
+                       (o, (b, n, hq, d), "o")):
+        _check(t, shp, q.dtype, q.device, nm)
+    _check(lse, (b, hq, n), torch.float32, q.device, "lse")
+    st = lib.attn_fwd_standard(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(workspace),
+                               _check_ws(workspace, q.device), b, n, hq, hkv, d, _dtype_code(q),
+                               int(bool(causal)), float(scale), _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_fwd_standard")
+
+
+def attn_bwd_standard(q, k, v, dout, dq, dk, dv, workspace, causal: bool, scale: float, stream=None) -> None:
+    """Enqueue standard attention's backward pass, which reads the P that
+    ``attn_fwd_standard`` left in the same ``workspace``."""
+    lib = load_library()
+    b, n, hq, hkv, d = _dims(q, k)
+    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, n, hkv, d), "k"), (v, (b, n, hkv, d), "v"),
+                       (dout, (b, n, hq, d), "dout"), (dq, (b, n, hq, d), "dq"),
+                       (dk, (b, n, hkv, d), "dk"), (dv, (b, n, hkv, d), "dv")):
+        _check(t, shp, q.dtype, q.device, nm)
+    st = lib.attn_bwd_standard(_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                               _ptr(workspace), _check_ws(workspace, q.device), b, n, hq, hkv, d,
+                               _dtype_code(q), int(bool(causal)), float(scale), _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_standard")
+
+
+def standard_probs(workspace, b: int, n: int, hq: int, dtype):
+    """The materialised P [B, Hq, N, N] inside a standard-attention workspace
+    (a view; layout as include/attn.h states it: row pitch N rounded up to 64,
+    after the fp32 score matrix rounded up to 256 bytes)."""
+    ldn = -(-n // 64) * 64
+    elems = b * hq * n * ldn
+    p_off = -(-(4 * elems) // 256) * 256
+    return workspace[p_off:p_off + 2 * elems].view(dtype).view(b, hq, n, ldn)[..., :n]
 
 
 def _default_scale(d: int, scale):

@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
-SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_bwd.hip")
+SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_std.hip")
 # Per-file extra flags.  The forward kernel never produces NaN from finite
 # inputs (masked scores are -inf, never NaN), so NaN-preserving max semantics
 # are dropped there: v_max3 then needs no canonicalising v_max per MFMA result.

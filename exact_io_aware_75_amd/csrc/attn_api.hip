@@ -303,6 +303,110 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
 #undef ATTN_BWD_ARGS
 #undef ATTN_BWD_PASS
 
+}  // extern "C"
+
+// ---- standard (materialising) attention ----
+
+namespace attn {
+
+StdWorkspace std_workspace_layout(int B, int N, int Hq) {
+  StdWorkspace w;
+  w.ldn = (N + 63) / 64 * 64;
+  const size_t elems = (size_t)B * Hq * N * w.ldn;
+  w.s_off = 0;
+  w.p_off = align256(w.s_off + elems * sizeof(float));
+  w.ds_off = align256(w.p_off + elems * sizeof(uint16_t));
+  w.total = align256(w.ds_off + elems * sizeof(uint16_t));
+  return w;
+}
+
+}  // namespace attn
+
+namespace {
+
+// Launch limits of the standard path: one row workgroup per (batch, head,
+// query row) in grid x, one (batch, head) per grid z of the tile products.
+int check_std_grid(int B, int N, int Hq) {
+  if ((long long)B * Hq * N >= (1LL << 24) || (long long)B * Hq > 65535) return ATTN_ERR_TOO_LARGE;
+  return ATTN_OK;
+}
+
+int std_common(bool fwd, const void* q, const void* k, const void* v, const void* dout, void* o,
+               float* lse, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, int B,
+               int N, int Hq, int Hkv, int d, int dtype, int causal, float scale, void* stream) {
+  if (!q || !k || !v) return ATTN_ERR_NULLPTR;
+  if (fwd ? (!o || !lse) : (!dout || !dq || !dk || !dv)) return ATTN_ERR_NULLPTR;
+  int st = check_shape(B, N, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  st = check_std_grid(B, N, Hq);
+  if (st != ATTN_OK) return st;
+  if (dtype != ATTN_DTYPE_FP16 && dtype != ATTN_DTYPE_BF16) return ATTN_ERR_DTYPE;
+  const void* ptrs[] = {q, k, v, fwd ? (const void*)o : dout, fwd ? (const void*)lse : dq,
+                        fwd ? nullptr : dk, fwd ? nullptr : dv};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return ATTN_ERR_ALIGN;
+  if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
+  const attn::StdWorkspace ws = attn::std_workspace_layout(B, N, Hq);
+  if (!workspace || workspace_bytes < ws.total) return ATTN_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+
+  attn::StdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.o = o;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.lse = lse;
+  char* w = static_cast<char*>(workspace);
+  a.s = reinterpret_cast<float*>(w + ws.s_off);
+  a.p = reinterpret_cast<uint16_t*>(w + ws.p_off);
+  a.ds = reinterpret_cast<uint16_t*>(w + ws.ds_off);
+  a.B = B;
+  a.N = N;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.d = d;
+  a.ldn = ws.ldn;
+  a.causal = causal != 0;
+  a.scale = scale;
+  const bool bf16 = dtype == ATTN_DTYPE_BF16;
+  hipError_t e = fwd ? attn::launch_std_fwd(a, bf16, static_cast<hipStream_t>(stream))
+                     : attn::launch_std_bwd(a, bf16, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t attn_standard_workspace_bytes(int B, int N, int Hq, int Hkv, int d) {
+  if (check_shape(B, N, Hq, Hkv, d) != ATTN_OK || check_std_grid(B, N, Hq) != ATTN_OK) return 0;
+  return attn::std_workspace_layout(B, N, Hq).total;
+}
+
+int attn_fwd_standard(const void* q, const void* k, const void* v, void* o, float* lse, void* workspace,
+                      size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype, int causal,
+                      float scale, void* stream) {
+  return std_common(true, q, k, v, nullptr, o, lse, nullptr, nullptr, nullptr, workspace, workspace_bytes,
+                    B, N, Hq, Hkv, d, dtype, causal, scale, stream);
+}
+
+int attn_bwd_standard(const void* q, const void* k, const void* v, const void* dout, void* dq, void* dk,
+                      void* dv, void* workspace, size_t workspace_bytes, int B, int N, int Hq, int Hkv,
+                      int d, int dtype, int causal, float scale, void* stream) {
+  return std_common(false, q, k, v, dout, nullptr, nullptr, dq, dk, dv, workspace, workspace_bytes, B, N,
+                    Hq, Hkv, d, dtype, causal, scale, stream);
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";

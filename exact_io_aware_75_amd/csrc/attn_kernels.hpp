@@ -79,4 +79,48 @@ SplitWorkspace split_workspace_layout(int B, int N, int Hq, int d, int splits);
 hipError_t launch_bwd(const BwdArgs& a, bool bf16, int d, bool causal, int stage_mask,
                       hipStream_t stream);
 
+// ---- standard (materialising) attention ----
+// One operand of the standard path's tile product (16-bit elements).
+struct StdOperand {
+  const uint16_t* p;
+  long long bstride, hstride;  // elements between batches / heads
+  int ld;                      // elements between consecutive stored rows
+  int hmul, hdiv;              // head of stage s for output head ho: (ho * hmul + s) / hdiv
+  int xext;                    // extent of the operand's own (non-reduction) index
+};
+struct StdGemmArgs {
+  StdOperand a, b;
+  void* c;                     // fp32 or 16-bit output
+  long long c_bstride, c_hstride;
+  int c_ld;
+  int M, Nn, K;                // C is M x Nn, reduction length K per stage
+  int Hout, nsum;              // output heads; stages summed per output head
+  float alpha;
+};
+struct StdRowArgs {
+  float* s;        // S or dP rows, fp32, pitch ldn
+  uint16_t* p;     // P rows
+  uint16_t* ds;    // dS rows
+  float* lse;      // [B, Hq, N]
+  int N, ldn, causal;
+};
+struct StdArgs {
+  const void *q, *k, *v, *dout;
+  void *o, *dq, *dk, *dv;
+  float* lse;
+  float* s;        // [B, Hq, N, ldn] fp32: S, later dP
+  uint16_t* p;     // [B, Hq, N, ldn]: P
+  uint16_t* ds;    // [B, Hq, N, ldn]: dS
+  int B, N, Hq, Hkv, d, ldn, causal;
+  float scale;
+};
+// Workspace layout of the standard path (offsets in bytes, 256-byte aligned).
+struct StdWorkspace {
+  int ldn;
+  size_t s_off, p_off, ds_off, total;
+};
+StdWorkspace std_workspace_layout(int B, int N, int Hq);
+hipError_t launch_std_fwd(const StdArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_std_bwd(const StdArgs& a, bool bf16, hipStream_t stream);
+
 }  // namespace attn

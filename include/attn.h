@@ -229,6 +229,48 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
                          size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
                          int causal, float scale, void* stream);
 
+/*
+ * Standard (materialising) attention: the baseline the pages measure the
+ * IO-aware method against (FlashAttention-1 news page, "FlashAttention"
+ * section: standard attention writes the N x N attention matrix to HBM and
+ * reads it back; FlashAttention-2 review, "Введение").  Same result and the
+ * same arguments, layouts and error behaviour as attn_fwd / attn_bwd, but
+ * every intermediate goes through device memory, in separate launches:
+ *
+ *   attn_fwd_standard   S = scale q k^T  (float32, full N x N per head)
+ *                       P = softmax(S) row-wise with the causal mask applied
+ *                           (masked entries stored as 0), rounded to dtype;
+ *                           lse = per-row natural-log log-sum-exp
+ *                       o = P v
+ *   attn_bwd_standard   dv = P^T dout,  dP = dout v^T  (float32, over S),
+ *                       dS = P * (dP - rowsum(P * dP))  (rounded to dtype),
+ *                       dq = scale dS k,  dk = scale dS^T q
+ *                       (dk / dv of a K/V head sum the heads of its group)
+ *
+ * `workspace` (device memory, 16-byte aligned, at least
+ * attn_standard_workspace_bytes() bytes) holds the materialised matrices,
+ * each [B, Hq, N, ldn] row-major with row pitch ldn = N rounded up to a
+ * multiple of 64:
+ *     byte 0                                S, then dP    float32
+ *     p_off  = 4 * E rounded up to 256      P             dtype
+ *     ds_off = p_off + 2 * E, rounded up    dS            dtype
+ * with E = B * Hq * N * ldn, i.e. O(N^2) memory, against O(N) for attn_bwd's
+ * workspace.  attn_bwd_standard reads the P that attn_fwd_standard left in
+ * the same workspace (standard attention keeps P for the backward pass), so
+ * the two calls must use one workspace, be ordered on one stream and use the
+ * same inputs, causal flag and scale.  Limits: B * Hq * N < 2^24 and
+ * B * Hq <= 65535 (ATTN_ERR_TOO_LARGE otherwise).
+ */
+size_t attn_standard_workspace_bytes(int B, int N, int Hq, int Hkv, int d);
+
+int attn_fwd_standard(const void* q, const void* k, const void* v, void* o, float* lse,
+                      void* workspace, size_t workspace_bytes, int B, int N, int Hq, int Hkv,
+                      int d, int dtype, int causal, float scale, void* stream);
+
+int attn_bwd_standard(const void* q, const void* k, const void* v, const void* dout, void* dq,
+                      void* dk, void* dv, void* workspace, size_t workspace_bytes, int B, int N,
+                      int Hq, int Hkv, int d, int dtype, int causal, float scale, void* stream);
+
 /* Static, human-readable description of a status code. */
 const char* attn_strerror(int status);
 

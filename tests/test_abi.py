@@ -189,3 +189,37 @@ def test_splitkv_rejects_invalid_arguments(lib):
     assert f(ws_bytes=need - 1) == c["ATTN_ERR_WORKSPACE"]
     assert f(ws=A + 4) == c["ATTN_ERR_ALIGN"]
     assert f(q=None) == c["ATTN_ERR_NULLPTR"]
+
+
+def test_standard_rejects_invalid_arguments(lib):
+    c = _status_codes()
+    need = lib.attn_standard_workspace_bytes(1, 100, 2, 1, 64)
+    # S (fp32), P and dS (16-bit), each [B, Hq, N, ldn] with ldn = 128, 256-byte aligned
+    assert need == 4 * 2 * 100 * 128 + 2 * (2 * 2 * 100 * 128)
+    assert lib.attn_standard_workspace_bytes(1, 100, 3, 2, 64) == 0
+    assert lib.attn_standard_workspace_bytes(1, 1 << 20, 32, 32, 64) == 0  # B * Hq * N >= 2^24
+    fwd = lambda ws=A, ws_bytes=need, o=A, N=100, d=64, scale=0.125: lib.attn_fwd_standard(  # noqa: E731
+        A, A, A, o, A, ws, ws_bytes, 1, N, 2, 1, d, 1, 1, scale, None)
+    assert fwd(o=None) == c["ATTN_ERR_NULLPTR"]
+    assert fwd(ws=None) == c["ATTN_ERR_WORKSPACE"]
+    assert fwd(ws_bytes=need - 1) == c["ATTN_ERR_WORKSPACE"]
+    assert fwd(ws=A + 8) == c["ATTN_ERR_ALIGN"]
+    assert fwd(o=A + 2) == c["ATTN_ERR_ALIGN"]
+    assert fwd(d=32) == c["ATTN_ERR_HEADDIM"]
+    assert fwd(N=0) == c["ATTN_ERR_SHAPE"]
+    assert fwd(N=1 << 23) == c["ATTN_ERR_TOO_LARGE"]
+    assert fwd(scale=math.nan) == c["ATTN_ERR_SCALE"]
+    bwd = lambda dq=A, ws_bytes=need: lib.attn_bwd_standard(  # noqa: E731
+        A, A, A, A, dq, A, A, A, ws_bytes, 1, 100, 2, 1, 64, 0, 0, 0.125, None)
+    assert bwd(dq=None) == c["ATTN_ERR_NULLPTR"]
+    assert bwd(ws_bytes=need - 1) == c["ATTN_ERR_WORKSPACE"]
+
+
+def test_standard_workspace_is_quadratic_in_sequence_length(lib):
+    """The materialising baseline needs O(N^2) memory (FlashAttention-1 news
+    page, "FlashAttention": standard attention keeps the N x N matrix in HBM),
+    against the tiled path's O(N)."""
+    f = lambda n: lib.attn_standard_workspace_bytes(1, n, 4, 4, 64)  # noqa: E731
+    for n in (1024, 2048, 4096):
+        assert f(n) == 4 * n * n * (4 + 2 + 2)
+        assert f(n) / lib.attn_bwd_workspace_bytes(1, n, 4, 4, 64) == 2 * n
