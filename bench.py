@@ -30,6 +30,9 @@ Prints one JSON line.  Besides the throughput it carries
                 split-KV forward (attn_fwd_splitkv) on a short-query shape,
                 128 queries against 65536 keys, B = 1, H = 32, d = 128,
                 against the unsplit kernel;
+  mfma_ceiling  the sustained MFMA rate measured on this part by
+                libattn_probe.so (random and constant bf16 operands); the
+                roofline entry also gives the dominant kernel's fraction of it;
   standard      standard attention (attn_fwd_standard / attn_bwd_standard),
                 which writes the N x N scores and probabilities to HBM, against
                 the tiled kernels on the step's shape: times, speed-ups, extra
@@ -229,6 +232,9 @@ def run(args):
         line["shard"] = shard_measure()
     if args.standard:
         line["standard"] = standard_measure()
+    ceil = mfma_ceiling()
+    line["mfma_ceiling"] = ceil
+    roofline["frac_of_measured_ceiling"] = round(achieved / ceil["random_bf16_tflops"], 4)
     if args.sweep:
         sweep()
     if args.cpu_seconds > 0:
@@ -452,6 +458,49 @@ def standard_measure():
     return out
 
 
+def mfma_ceiling():
+    """Sustained MFMA rate of this part (libattn_probe.so): back-to-back
+    32x32x16 bf16 products at two wavefronts per SIMD on every CU, once on
+    random bf16 operands (the realistic ceiling: the power-limited clock
+    depends on operand bit toggling) and once on constant operands."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_io_aware_75_amd", "libattn_probe.so"))
+    lib.attn_probe_mfma.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.attn_probe_mfma.restype = ctypes.c_int
+    lib.attn_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    lib.attn_probe_mfma_flops.restype = ctypes.c_double
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    wgs, iters = 256 * 2, 20000  # two four-wavefront workgroups per CU: two wavefronts per SIMD
+    out = torch.empty(wgs * 256 * 16, dtype=torch.float32, device=dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    res = {}
+    for kind in ("random", "constant"):
+        if kind == "random":
+            ops = torch.randn(wgs * 256 * 64, device=dev, generator=g).to(torch.bfloat16)
+        else:
+            ops = torch.full((wgs * 256 * 64,), 0.5, device=dev, dtype=torch.bfloat16)
+
+        def call():
+            st = lib.attn_probe_mfma(ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(out.data_ptr()), wgs, iters,
+                                     ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"attn_probe_mfma failed with status {st}")
+
+        t = _median_ms(call, stream, reps=5)
+        res[kind] = lib.attn_probe_mfma_flops(wgs, iters) / (t / 1e3) / 1e12
+    del out, ops
+    torch.cuda.empty_cache()
+    return {"what": "v_mfma_f32_32x32x16_bf16 back to back, 2 wavefronts per SIMD on all 256 CUs",
+            "random_bf16_tflops": round(res["random"], 1), "constant_tflops": round(res["constant"], 1),
+            "frac_of_spec_random": round(res["random"] / PEAK_BF16_TFLOPS, 4)}
+
+
 def mk_shape(g, dev, b, n, h, d):
     import torch
 
@@ -580,6 +629,50 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
     print("\n".join(lines))
 
 
+def summarize_hbm(trace_dir, fetch_dir, write_dir, out_name, title, cmds, name_filter):
+    """Write profiles/<out_name>: mean duration (kernel trace), HBM bytes read
+    and written per launch (FETCH_SIZE / WRITE_SIZE runs, scaled by the same
+    counters' reading for the calibration copy) and the resulting GB/s for the
+    kernels whose name holds `name_filter`."""
+    import glob
+
+    def find(d, pattern):
+        hits = sorted(glob.glob(os.path.join(d, "**", pattern), recursive=True))
+        if not hits:
+            raise SystemExit(f"no {pattern} under {d}")
+        return hits[0]
+
+    def per_kernel(d, counter):
+        acc = {}
+        for r in _read_csv(find(d, "*counter_collection.csv")):
+            if r.get("Counter_Name") == counter:
+                acc.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k_: sum(v_) / len(v_) for k_, v_ in acc.items()}
+
+    fetch, write = per_kernel(fetch_dir, "FETCH_SIZE"), per_kernel(write_dir, "WRITE_SIZE")
+    cname = next(k_ for k_ in fetch if "elementwise" in k_.lower() and "neg" in k_.lower())
+    f_scale = COPY_BYTES / (fetch[cname] * 1024.0)
+    w_scale = COPY_BYTES / (write[cname] * 1024.0)
+    lines = [title, ""] + [f"{k_}: {v_}" for k_, v_ in cmds.items()] + [
+        "", f"HBM counter calibration: plain copy of {COPY_BYTES} B -> byte scale {f_scale:.4f} (fetch) / "
+            f"{w_scale:.4f} (write)", "",
+        f"{'kernel':58s} {'calls':>5s} {'avg_us':>9s} {'HBM_rd_MB':>10s} {'HBM_wr_MB':>10s} {'HBM_GB/s':>9s}"]
+    for r in _read_csv(find(trace_dir, "*kernel_stats.csv")):
+        nm = r["Name"]
+        if name_filter not in nm:
+            continue
+        avg_us = float(r["AverageNs"]) / 1e3
+        rd = fetch.get(nm, float("nan")) * 1024.0 * f_scale
+        wr = write.get(nm, float("nan")) * 1024.0 * w_scale
+        short = nm.replace("(anonymous namespace)::", "").replace("attn::", "").replace("void ", "")
+        short = short[:short.find("(")]
+        lines.append(f"{short[:58]:58s} {r['Calls']:>5s} {avg_us:9.2f} {rd / 1e6:10.1f} {wr / 1e6:10.1f} "
+                     f"{(rd + wr) / (avg_us * 1e-6) / 1e9:9.1f}")
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_trace(trace_dir, out_name, title, cmd, name_filter=""):
     """Write profiles/<out_name>: calls and durations per kernel and grid shape
     of a rocprofv3 --kernel-trace run (its kernel_trace.csv), for the kernels
@@ -635,9 +728,15 @@ def main():
     ap.add_argument("--summarize-trace", nargs=4, metavar=("TRACE_DIR", "OUT_NAME", "TITLE", "CMD"),
                     help="write a per-kernel duration table of a kernel-trace run to profiles/OUT_NAME and exit")
     ap.add_argument("--trace-filter", default="", help="only kernels whose name contains this")
+    ap.add_argument("--summarize-hbm", nargs=6, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "OUT_NAME", "TITLE",
+                                                        "FILTER"),
+                    help="write per-kernel time and HBM bytes of matching kernels to profiles/OUT_NAME and exit")
     args = ap.parse_args()
     if args.summarize:
         summarize_profiles(*args.summarize, json.loads(args.summarize_cmds))
+        return
+    if args.summarize_hbm:
+        summarize_hbm(*args.summarize_hbm[:5], json.loads(args.summarize_cmds), args.summarize_hbm[5])
         return
     if args.summarize_trace:
         summarize_trace(*args.summarize_trace, name_filter=args.trace_filter)

@@ -3,7 +3,8 @@
     python -m exact_io_aware_75_amd.build        # or __graft_entry__.build()
 
 Each HIP source is compiled to an object under _build/ and linked into
-exact_io_aware_75_amd/libattn.so.  Always recompiles (the build is the
+exact_io_aware_75_amd/libattn.so (the attention library) or
+exact_io_aware_75_amd/libattn_probe.so (the MFMA throughput probe).  Always recompiles (the build is the
 "does it build" check).
 """
 
@@ -19,6 +20,9 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_std.hip")
+# The MFMA throughput probe the benchmark measures its ceiling with: a
+# separate library, not part of the attention ABI.
+PROBE_SOURCES = ("mfma_probe.hip",)
 # Per-file extra flags.  The forward kernel never produces NaN from finite
 # inputs (masked scores are -inf, never NaN), so NaN-preserving max semantics
 # are dropped there: v_max3 then needs no canonicalising v_max per MFMA result.
@@ -26,6 +30,7 @@ SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_std.hip")
 # keeps full IEEE semantics.
 FILE_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"]}
 LIB = os.path.join(HERE, "libattn.so")
+PROBE_LIB = os.path.join(HERE, "libattn_probe.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -48,18 +53,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=min(len(SOURCES), 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=min(len(srcs), 5)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s_] for s_ in SOURCES], LIB)
+    _link([objs[s_] for s_ in PROBE_SOURCES], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -210,13 +210,26 @@ __device__ __forceinline__ float block_reduce(float x, float* red) {
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// The row kernels read each row from HBM once when it fits in registers:
+// CAP floats per thread (row pitch ldn <= 256 CAP), chunk t of thread tid at
+// column 4 tid + 1024 t.  CAP = 0 streams the row once per pass instead.
+__device__ __forceinline__ float pe_of(Bf16Tag, u32x2_t w, int e) { return to_float(Bf16Tag{}, (uint16_t)(w[e >> 1] >> (16 * (e & 1)))); }
+__device__ __forceinline__ float pe_of(F16Tag, u32x2_t w, int e) { return to_float(F16Tag{}, (uint16_t)(w[e >> 1] >> (16 * (e & 1)))); }
+
+template <typename Tag>
+__device__ __forceinline__ u32x2_t pack4(const float* x) {
+  return (u32x2_t){(uint32_t)to_bits(Tag{}, x[0]) | ((uint32_t)to_bits(Tag{}, x[1]) << 16),
+                   (uint32_t)to_bits(Tag{}, x[2]) | ((uint32_t)to_bits(Tag{}, x[3]) << 16)};
+}
+
 // One workgroup per (batch, head, query row i): P[i, :] = softmax of the
 // allowed entries of S[i, :] (keys j < N, and j <= i when causal), stored in
 // the 16-bit type with zeros elsewhere (up to the row pitch), and
 // LSE[i] = max + ln(sum).
-template <typename Tag>
+template <typename Tag, int CAP>
 __global__ void __launch_bounds__(GTHREADS) std_softmax_kernel(StdRowArgs a) {
   __shared__ float red[GTHREADS / 64];
+  constexpr int NC = CAP > 0 ? CAP / 4 : 1;
   const int row = blockIdx.x;  // (b * Hq + h) * N + i
   const int i = row % a.N;
   const int nvis = a.causal ? min(i + 1, a.N) : a.N;
@@ -224,31 +237,63 @@ __global__ void __launch_bounds__(GTHREADS) std_softmax_kernel(StdRowArgs a) {
   uint16_t* p = a.p + (size_t)row * a.ldn;
   const int tid = threadIdx.x;
 
+  f32x4_t c[NC];
   float m = -INFINITY;
-  for (int j = 4 * tid; j < nvis; j += 4 * GTHREADS) {
-    const f32x4_t v = *(const f32x4_t*)(s + j);
+  if constexpr (CAP > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) m = (j + e < nvis) ? fmaxf(m, v[e]) : m;
+    for (int t = 0; t < NC; ++t) {
+      const int j = 4 * tid + 4 * GTHREADS * t;
+      c[t] = j < nvis ? *(const f32x4_t*)(s + j) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = (j + e < nvis) ? fmaxf(m, c[t][e]) : m;
+    }
+  } else {
+    for (int j = 4 * tid; j < nvis; j += 4 * GTHREADS) {
+      const f32x4_t v = *(const f32x4_t*)(s + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = (j + e < nvis) ? fmaxf(m, v[e]) : m;
+    }
   }
   m = block_reduce<true>(m, red);
   float l = 0.f;
-  for (int j = 4 * tid; j < nvis; j += 4 * GTHREADS) {
-    const f32x4_t v = *(const f32x4_t*)(s + j);
+  if constexpr (CAP > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) l += (j + e < nvis) ? fast_exp2((v[e] - m) * LOG2E) : 0.f;
+    for (int t = 0; t < NC; ++t) {
+      const int j = 4 * tid + 4 * GTHREADS * t;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[t][e] = (j + e < nvis) ? fast_exp2((c[t][e] - m) * LOG2E) : 0.f;
+        l += c[t][e];
+      }
+    }
+  } else {
+    for (int j = 4 * tid; j < nvis; j += 4 * GTHREADS) {
+      const f32x4_t v = *(const f32x4_t*)(s + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l += (j + e < nvis) ? fast_exp2((v[e] - m) * LOG2E) : 0.f;
+    }
   }
   l = block_reduce<false>(l, red);
   const float inv = 1.0f / l;
-  for (int j = 4 * tid; j < a.ldn; j += 4 * GTHREADS) {
-    float pe[4] = {0.f, 0.f, 0.f, 0.f};
-    if (j < nvis) {
-      const f32x4_t v = *(const f32x4_t*)(s + j);
+  if constexpr (CAP > 0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pe[e] = (j + e < nvis) ? fast_exp2((v[e] - m) * LOG2E) * inv : 0.f;
+    for (int t = 0; t < NC; ++t) {
+      const int j = 4 * tid + 4 * GTHREADS * t;
+      if (j < a.ldn) {
+        const float pe[4] = {c[t][0] * inv, c[t][1] * inv, c[t][2] * inv, c[t][3] * inv};
+        *(u32x2_t*)(p + j) = pack4<Tag>(pe);
+      }
     }
-    const uint32_t w0 = (uint32_t)to_bits(Tag{}, pe[0]) | ((uint32_t)to_bits(Tag{}, pe[1]) << 16);
-    const uint32_t w1 = (uint32_t)to_bits(Tag{}, pe[2]) | ((uint32_t)to_bits(Tag{}, pe[3]) << 16);
-    *(u32x2_t*)(p + j) = (u32x2_t){w0, w1};
+  } else {
+    for (int j = 4 * tid; j < a.ldn; j += 4 * GTHREADS) {
+      float pe[4] = {0.f, 0.f, 0.f, 0.f};
+      if (j < nvis) {
+        const f32x4_t v = *(const f32x4_t*)(s + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) pe[e] = (j + e < nvis) ? fast_exp2((v[e] - m) * LOG2E) * inv : 0.f;
+      }
+      *(u32x2_t*)(p + j) = pack4<Tag>(pe);
+    }
   }
   if (tid == 0) a.lse[row] = m + fast_log2(l) * LN2;
 }
@@ -256,40 +301,76 @@ __global__ void __launch_bounds__(GTHREADS) std_softmax_kernel(StdRowArgs a) {
 // One workgroup per (batch, head, query row i): D = sum_j P[i, j] dP[i, j]
 // over the keys j < N, then dS[i, j] = P[i, j] (dP[i, j] - D) in the 16-bit
 // type, zeros past N.
-template <typename Tag>
+template <typename Tag, int CAP>
 __global__ void __launch_bounds__(GTHREADS) std_softmax_bwd_kernel(StdRowArgs a) {
   __shared__ float red[GTHREADS / 64];
+  constexpr int NC = CAP > 0 ? CAP / 4 : 1;
   const int row = blockIdx.x;
   const float* dp = a.s + (size_t)row * a.ldn;
   const uint16_t* p = a.p + (size_t)row * a.ldn;
   uint16_t* ds = a.ds + (size_t)row * a.ldn;
   const int tid = threadIdx.x;
+  f32x4_t cdp[NC];
+  u32x2_t cp[NC];
   float dsum = 0.f;
-  for (int j = 4 * tid; j < a.N; j += 4 * GTHREADS) {
-    const f32x4_t v = *(const f32x4_t*)(dp + j);
-    const u32x2_t w = *(const u32x2_t*)(p + j);
+  if constexpr (CAP > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float pe = to_float(Tag{}, (uint16_t)(w[e >> 1] >> (16 * (e & 1))));
-      dsum += (j + e < a.N) ? pe * v[e] : 0.f;
+    for (int t = 0; t < NC; ++t) {
+      const int j = 4 * tid + 4 * GTHREADS * t;
+      const bool in = j < a.N;
+      cdp[t] = in ? *(const f32x4_t*)(dp + j) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      cp[t] = in ? *(const u32x2_t*)(p + j) : (u32x2_t){0u, 0u};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dsum += (j + e < a.N) ? pe_of(Tag{}, cp[t], e) * cdp[t][e] : 0.f;
     }
-  }
-  const float D = block_reduce<false>(dsum, red);
-  for (int j = 4 * tid; j < a.ldn; j += 4 * GTHREADS) {
-    float o[4] = {0.f, 0.f, 0.f, 0.f};
-    if (j < a.N) {
+  } else {
+    for (int j = 4 * tid; j < a.N; j += 4 * GTHREADS) {
       const f32x4_t v = *(const f32x4_t*)(dp + j);
       const u32x2_t w = *(const u32x2_t*)(p + j);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float pe = to_float(Tag{}, (uint16_t)(w[e >> 1] >> (16 * (e & 1))));
-        o[e] = (j + e < a.N) ? pe * (v[e] - D) : 0.f;
+      for (int e = 0; e < 4; ++e) dsum += (j + e < a.N) ? pe_of(Tag{}, w, e) * v[e] : 0.f;
+    }
+  }
+  const float D = block_reduce<false>(dsum, red);
+  if constexpr (CAP > 0) {
+#pragma unroll
+    for (int t = 0; t < NC; ++t) {
+      const int j = 4 * tid + 4 * GTHREADS * t;
+      if (j < a.ldn) {
+        float o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (j + e < a.N) ? pe_of(Tag{}, cp[t], e) * (cdp[t][e] - D) : 0.f;
+        *(u32x2_t*)(ds + j) = pack4<Tag>(o);
       }
     }
-    const uint32_t w0 = (uint32_t)to_bits(Tag{}, o[0]) | ((uint32_t)to_bits(Tag{}, o[1]) << 16);
-    const uint32_t w1 = (uint32_t)to_bits(Tag{}, o[2]) | ((uint32_t)to_bits(Tag{}, o[3]) << 16);
-    *(u32x2_t*)(ds + j) = (u32x2_t){w0, w1};
+  } else {
+    for (int j = 4 * tid; j < a.ldn; j += 4 * GTHREADS) {
+      float o[4] = {0.f, 0.f, 0.f, 0.f};
+      if (j < a.N) {
+        const f32x4_t v = *(const f32x4_t*)(dp + j);
+        const u32x2_t w = *(const u32x2_t*)(p + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = (j + e < a.N) ? pe_of(Tag{}, w, e) * (v[e] - D) : 0.f;
+      }
+      *(u32x2_t*)(ds + j) = pack4<Tag>(o);
+    }
   }
+}
+
+// Launch a row kernel with the register capacity that holds a row of pitch ldn.
+template <typename Tag, int CAP>
+hipError_t launch_rows(bool fwd, const StdRowArgs& r, int rows, hipStream_t st) {
+  if (fwd) hipLaunchKernelGGL((std_softmax_kernel<Tag, CAP>), dim3(rows), dim3(GTHREADS), 0, st, r);
+  else hipLaunchKernelGGL((std_softmax_bwd_kernel<Tag, CAP>), dim3(rows), dim3(GTHREADS), 0, st, r);
+  return hipGetLastError();
+}
+
+template <typename Tag>
+hipError_t row_pass(bool fwd, const StdRowArgs& r, int rows, hipStream_t st) {
+  if (r.ldn <= 4 * GTHREADS) return launch_rows<Tag, 4>(fwd, r, rows, st);
+  if (r.ldn <= 16 * GTHREADS) return launch_rows<Tag, 16>(fwd, r, rows, st);
+  if (r.ldn <= 64 * GTHREADS) return launch_rows<Tag, 64>(fwd, r, rows, st);
+  return launch_rows<Tag, 0>(fwd, r, rows, st);
 }
 
 template <typename Tag, bool AT, bool BT, bool OUT_F32>
@@ -340,8 +421,7 @@ hipError_t std_fwd(const StdArgs& a, hipStream_t st) {
               a.s, mb, mh, a.ldn, d, a.Hq, 1, a.scale), a.B, st);
   if (e != hipSuccess) return e;
   StdRowArgs r{a.s, a.p, a.ds, a.lse, N, a.ldn, a.causal};
-  hipLaunchKernelGGL((std_softmax_kernel<Tag>), dim3(a.B * a.Hq * N), dim3(GTHREADS), 0, st, r);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = row_pass<Tag>(true, r, a.B * a.Hq * N, st)) != hipSuccess) return e;
   // O = P V: V is the B operand with its key (reduction) index as rows
   return gemm<Tag, false, true, false>(
       product(operand(a.p, mb, mh, a.ldn, 1, 1, N), operand(a.v, kb, d, a.Hkv * d, 1, grp, d),
@@ -365,8 +445,7 @@ hipError_t std_bwd(const StdArgs& a, hipStream_t st) {
               a.s, mb, mh, a.ldn, d, a.Hq, 1, 1.0f), a.B, st);
   if (e != hipSuccess) return e;
   StdRowArgs r{a.s, a.p, a.ds, a.lse, N, a.ldn, a.causal};
-  hipLaunchKernelGGL((std_softmax_bwd_kernel<Tag>), dim3(a.B * a.Hq * N), dim3(GTHREADS), 0, st, r);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = row_pass<Tag>(false, r, a.B * a.Hq * N, st)) != hipSuccess) return e;
   // dQ = scale dS K
   e = gemm<Tag, false, true, false>(
       product(operand(a.ds, mb, mh, a.ldn, 1, 1, N), operand(a.k, kb, d, a.Hkv * d, 1, grp, d),

@@ -223,3 +223,24 @@ def test_standard_workspace_is_quadratic_in_sequence_length(lib):
     for n in (1024, 2048, 4096):
         assert f(n) == 4 * n * n * (4 + 2 + 2)
         assert f(n) / lib.attn_bwd_workspace_bytes(1, n, 4, 4, 64) == 2 * n
+
+
+def test_probe_library_exports_its_header():
+    """libattn_probe.so (the benchmark's MFMA throughput probe) exports every
+    entry point include/attn_probe.h declares, and rejects bad arguments."""
+    path = os.path.join(ROOT, "exact_io_aware_75_amd", "libattn_probe.so")
+    if not os.path.exists(path):
+        from exact_io_aware_75_amd.build import build
+
+        build()
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "attn_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
+    assert names == ["attn_probe_mfma", "attn_probe_mfma_flops"]
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
+    for name in names:
+        assert re.search(rf"\bT {name}\b", out), name
+    lib = ctypes.CDLL(path)
+    lib.attn_probe_mfma_flops.restype = ctypes.c_double
+    assert lib.attn_probe_mfma_flops(2, 3) == 2 * 4 * 3 * 16 * 2 * 32 * 32 * 16
+    assert lib.attn_probe_mfma(None, ctypes.c_void_p(A), 1, 1, None) == 1
+    assert lib.attn_probe_mfma(ctypes.c_void_p(A), ctypes.c_void_p(A), 0, 1, None) == 2

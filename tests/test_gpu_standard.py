@@ -134,3 +134,36 @@ def test_full_size_matches_oracle_and_tiled_path(gpu_device):
             f"max|ddV|={max_err(dv[bi, :, g], rdv)[0]:.3e}")
         assert excess(dk[bi, :, g], rdk, TOL_GRAD, dtype) <= 0
         assert excess(dv[bi, :, g], rdv, TOL_GRAD, dtype) <= 0
+
+
+@pytest.mark.parametrize("n", [1500, 5000, 16400])
+def test_row_kernel_capacities(gpu_device, n):
+    """The row kernels keep a row in registers up to a pitch of 1024, 4096 or
+    16384 columns and stream it beyond that: one shape per regime, every
+    element against the tiled kernels and sampled rows against the oracle."""
+    import torch
+    import exact_io_aware_75_amd as ea
+
+    b, h, d, dtype, causal = 1, 2, 64, "bf16", True
+    x = gen.make_inputs(b, n, h, h, d, dtype, cfg_id=25)
+    scale = 1.0 / np.sqrt(d)
+    log(f"standard row capacity n={n}")
+    o, lse, dq, dk, dv, _ = run_standard(x, dtype, causal, scale, gpu_device)
+    q, k, v, do = (gen.to_torch(x[t], dtype, gpu_device) for t in ("q", "k", "v", "do"))
+    to, tlse = ea.forward(q, k, v, causal=causal, scale=scale)
+    tdq, tdk, tdv = ea.backward(q, k, v, to, tlse, do, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    f = lambda t: t.float().cpu().numpy().astype(np.float64)  # noqa: E731
+    for nm, a_, t_, tol in (("o", o, f(to), TOL_O), ("dq", dq, f(tdq), TOL_GRAD),
+                            ("dk", dk, f(tdk), TOL_GRAD), ("dv", dv, f(tdv), TOL_GRAD)):
+        assert np.isfinite(a_).all()
+        assert excess(a_, t_, 2 * tol, dtype) <= 0, nm
+    assert np.abs(lse - tlse.cpu().numpy()).max() <= 2 * TOL_LSE
+    rows = [0, n // 3, n - 1]
+    for hh in range(h):
+        args = (x["q"][0, :, hh], x["k"][0, :, hh], x["v"][0, :, hh])
+        ro, rl = oracle.attention_head_fwd(*args, causal, scale, rows=rows)
+        rdq, _, _ = oracle.attention_head_bwd(*args, x["do"][0, :, hh], causal, scale, rows=rows)
+        assert excess(o[0, rows, hh], ro, TOL_O, dtype) <= 0
+        assert np.abs(lse[0, hh, rows] - rl).max() <= TOL_LSE
+        assert excess(dq[0, rows, hh], rdq, TOL_GRAD, dtype) <= 0
