@@ -75,12 +75,22 @@ const attn::SparseArgs kDense = {nullptr, 0, 0};
 
 namespace attn {
 
-BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int /*Hkv*/, int d) {
+int bwd_head_split(int B, int Nk, int Hkv, int group, int d) {
+  const long long base = (long long)((Nk + 127) / 128) * Hkv * B;  // dK/dV workgroups unsplit
+  if (group <= 1 || base >= 512 || d > 128) return 1;
+  for (int s = 2; s < group; ++s)
+    if (group % s == 0 && base * s >= 1024) return s;
+  return group;
+}
+
+BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int Hkv, int d, bool with_split) {
   BwdWorkspace w;
-  (void)d;
   w.delta_off = 0;
   w.delta_bytes = (size_t)B * Hq * N * sizeof(float);
-  w.total = align256(w.delta_off + w.delta_bytes);
+  w.hsplit = with_split ? bwd_head_split(B, N, Hkv, Hq / Hkv, d) : 1;
+  w.part_off = align256(w.delta_off + w.delta_bytes);
+  w.part_bytes = w.hsplit > 1 ? (size_t)w.hsplit * 2 * B * N * Hkv * d * sizeof(float) : 0;
+  w.total = align256(w.part_off + w.part_bytes);
   return w;
 }
 
@@ -224,7 +234,9 @@ int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, int 
   for (const void* p : ptrs)
     if (!aligned16(p)) return ATTN_ERR_ALIGN;
   if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
-  const attn::BwdWorkspace ws = attn::bwd_workspace_layout(B, N, Hq, Hkv, d);
+  // the dK/dV head split serves the square dense pass only
+  const bool split_ok = block_mask == nullptr && mask_heads == 0 && Nk == N;
+  const attn::BwdWorkspace ws = attn::bwd_workspace_layout(B, N, Hq, Hkv, d, split_ok);
   if (!workspace || workspace_bytes < ws.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
   attn::SparseArgs sp = kDense;
@@ -256,6 +268,8 @@ int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, int 
   a.sp = sp;
   a.Nk = Nk;
   a.coff = clamp_offset(causal_offset, N, Nk);
+  a.hsplit = ws.hsplit;
+  a.dkv_part = ws.hsplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_off) : nullptr;
   hipError_t e = attn::launch_bwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0, stages,
                                   static_cast<hipStream_t>(stream));
   if (e != hipSuccess) {

@@ -276,12 +276,19 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   const int half = lane >> 5;
   const int l32 = lane & 31;
 
-  // ---- which (batch, kv head, key block) this workgroup owns ----
+  // ---- which (batch, kv head, head split, key block) this workgroup owns ----
+  // (consecutive work items: consecutive key blocks of one head split, which
+  // stream the same query tiles)
+  // (d = 256 never splits: its registers are already full)
+  const int hs = D <= 128 ? a.hsplit : 1;
   const int nkb = (a.Nk + KV_BN - 1) / KV_BN;
-  const int total = nkb * a.Hkv * a.B;
+  const int total = nkb * a.Hkv * a.B * hs;
   const int Lw = xcd_remap(blockIdx.x, total);
-  const int bg = Lw / nkb;
-  const int kb = Lw - bg * nkb;
+  const int bgs = Lw / nkb;
+  const int kb = Lw - bgs * nkb;
+  const int bg = bgs / hs;
+  const int split = bgs - bg * hs;
+  const int gs = a.group / hs;  // query heads of the group this workgroup covers
   const int b = bg / a.Hkv;
   const int g = bg - b * a.Hkv;
   const int k0 = kb * KV_BN;           // first key of the block
@@ -341,7 +348,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     if (nlist > 0 && lds_uniform(blist, nlist - 1) == a.sp.nb - 1)
       tiles_per_head -= QPB - (a.N - (a.sp.nb - 1) * SPARSE_BLOCK + KV_BM - 1) / KV_BM;
   }
-  const int ntiles = tiles_per_head * a.group;
+  const int ntiles = tiles_per_head * gs;
   const float c = a.scale_log2;  // scale * log2(e), signed
 
   TileDma<D, KV_BM, W> qdma;
@@ -477,7 +484,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 
   // Tile t lives in buffer t & 1; one barrier per tile, the same number for
   // every wavefront.
-  int lh = g * a.group, lq = qfirst;  // coordinates of the next tile to load
+  int lh = g * a.group + split * gs, lq = qfirst;  // coordinates of the next tile to load
   if constexpr (SPARSE) lq = nlist > 0 ? lds_uniform(blist, 0) * SPARSE_BLOCK : 0;
   if (ntiles > 0) {
     load(lh, lq, q0s, o0s);
@@ -512,7 +519,23 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   if (t < ntiles) step(t, 0);
 
   // ---- epilogue: dK = scale * dK_acc, dV = dV_acc; lane = key, rows = d ----
-  if (mykey < a.Nk) {
+  if (hs > 1) {  // fp32 partials of this head split, summed by the reduce kernel
+    if (mykey < a.Nk) {
+      const size_t per = (size_t)a.B * a.Nk * a.Hkv * D;
+      float* pk = a.dkv_part + (size_t)split * 2 * per + (((size_t)b * a.Nk + mykey) * a.Hkv + g) * D;
+      float* pv = pk + per;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int d0 = 32 * db + 8 * q4 + 4 * half;
+          *(f32x4_t*)(pk + d0) = (f32x4_t){dk_acc[db][4 * q4], dk_acc[db][4 * q4 + 1], dk_acc[db][4 * q4 + 2],
+                                           dk_acc[db][4 * q4 + 3]};
+          *(f32x4_t*)(pv + d0) = (f32x4_t){dv_acc[db][4 * q4], dv_acc[db][4 * q4 + 1], dv_acc[db][4 * q4 + 2],
+                                           dv_acc[db][4 * q4 + 3]};
+        }
+    }
+  } else if (mykey < a.Nk) {
     uint16_t* dkp = (uint16_t*)a.dk + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)mykey * kv_row;
     uint16_t* dvp = (uint16_t*)a.dv + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)mykey * kv_row;
 #pragma unroll
@@ -787,6 +810,24 @@ attn_bwd_dq_kernel(BwdArgs a) {
 
 }  // namespace
 
+// dK = scale * sum of the head splits' partials, dV = sum, in split order
+// (deterministic); four elements per thread of the [B, Nk, Hkv, d] outputs.
+template <typename Tag, int D>
+__global__ void __launch_bounds__(256) attn_bwd_dkv_reduce_kernel(BwdArgs a) {
+  const size_t per = (size_t)a.B * a.Nk * a.Hkv * D;
+  const size_t i = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= per) return;
+  f32x4_t sk = {0.f, 0.f, 0.f, 0.f}, sv = {0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < a.hsplit; ++s) {
+    const float* p = a.dkv_part + (size_t)s * 2 * per + i;
+    sk += *(const f32x4_t*)p;
+    sv += *(const f32x4_t*)(p + per);
+  }
+  *(u32x2_t*)((uint16_t*)a.dk + i) = (u32x2_t){pack2(Tag{}, sk[0] * a.scale, sk[1] * a.scale),
+                                               pack2(Tag{}, sk[2] * a.scale, sk[3] * a.scale)};
+  *(u32x2_t*)((uint16_t*)a.dv + i) = (u32x2_t){pack2(Tag{}, sv[0], sv[1]), pack2(Tag{}, sv[2], sv[3])};
+}
+
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   if (SPARSE && (a.sp.bmask == nullptr || a.sp.nb != (a.N + SPARSE_BLOCK - 1) / SPARSE_BLOCK ||
@@ -803,12 +844,23 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   }
   if (stages & 2) {
     constexpr int W = DkdvWG<D, CAUSAL>::WAVES;
-    const long long grid = (long long)((a.Nk + 32 * W - 1) / (32 * W)) * a.Hkv * a.B;
+    if (a.hsplit < 1 || a.group % a.hsplit != 0 ||
+        (a.hsplit > 1 && (SPARSE || D > 128 || a.dkv_part == nullptr)))
+      return hipErrorInvalidValue;
+    const long long grid = (long long)((a.Nk + 32 * W - 1) / (32 * W)) * a.Hkv * a.B * a.hsplit;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (a.hsplit > 1) {
+      const long long n4 = ((long long)a.B * a.Nk * a.Hkv * D) / 4;
+      const long long rg = (n4 + 255) / 256;
+      if (rg > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      hipLaunchKernelGGL((attn_bwd_dkv_reduce_kernel<Tag, D>), dim3((unsigned)rg), dim3(256), 0, stream, a);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (stages & 4) {
     constexpr int W = DqWG<D, CAUSAL, SPARSE>::WAVES;

@@ -60,14 +60,29 @@ struct BwdArgs {
   float scale;       // signed softmax scale
   float scale_log2;  // scale * log2(e)
   SparseArgs sp;
+  // dK/dV pass over small grids: the query heads of each GQA group are split
+  // over `hsplit` workgroups per key block, which write fp32 partials
+  // [hsplit][2 (dK, dV)][B][Nk][Hkv][d] to dkv_part; a reduce kernel sums them
+  // (in split order) into dk, dv.  hsplit = 1: dk, dv written directly.
+  int hsplit;
+  float* dkv_part;
 };
 
 // Workspace layout of the backward pass (offsets in bytes, 256-byte aligned).
 struct BwdWorkspace {
   size_t delta_off, delta_bytes;
+  int hsplit;                   // head split of the dK/dV pass (1: none)
+  size_t part_off, part_bytes;  // fp32 dK/dV partials when hsplit > 1
   size_t total;
 };
-BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int Hkv, int d);
+// Head split of the dK/dV pass: 1 unless the pass would have fewer than 512
+// workgroups (B * Hkv * ceil(Nk / 128)), a group has several query heads and
+// d <= 128; then the smallest divisor of the group that gives >= 1024 (or
+// the group).
+int bwd_head_split(int B, int Nk, int Hkv, int group, int d);
+// with_split = false: the layout without the partials (rectangular and
+// block-sparse calls, which run unsplit).
+BwdWorkspace bwd_workspace_layout(int B, int N, int Hq, int Hkv, int d, bool with_split = true);
 
 hipError_t launch_fwd(const FwdArgs& a, bool bf16, int d, bool causal, hipStream_t stream);
 // Split-KV layout of the forward workspace (offsets in bytes, 256-byte aligned).

@@ -88,8 +88,15 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 
 /*
  * Bytes of device workspace attn_bwd needs for these sizes: the per-row
- * D = rowsum(dO * O) in float32, B * Hq * N values (O(B * N * Hq)), plus
- * alignment.  Returns 0 if the sizes are invalid.
+ * D = rowsum(dO * O) in float32, B * Hq * N values, plus alignment.  When
+ * the dK/dV pass would have few workgroups -- B * Hkv * ceil(N / 128) < 512,
+ * Hq > Hkv and d <= 128 (MQA/GQA with a small batch) -- the query heads of
+ * each group are split over `s` workgroups per key block (s the smallest
+ * divisor of Hq / Hkv with B * Hkv * ceil(N / 128) * s >= 1024, else
+ * Hq / Hkv) and the workspace also holds their float32 partial dK and dV,
+ * s * 2 * B * N * Hkv * d values, which are summed in a fixed order (the
+ * result stays deterministic).  Either way the size is O(N).  Returns 0 if
+ * the sizes are invalid.
  */
 size_t attn_bwd_workspace_bytes(int B, int N, int Hq, int Hkv, int d);
 

@@ -118,8 +118,16 @@ def test_workspace_is_linear_in_sequence_length(lib):
     # exact affine form up to 256-byte alignment padding
     assert abs((sizes[3] - sizes[2]) - 2 * (sizes[2] - sizes[1])) <= 512
     assert sizes[3] <= 4.01 * sizes[1]
-    # one fp32 per query row (D = rowsum(dO * O)), plus alignment padding
-    assert f(4096) <= 2 * 8 * 4096 * 4 + 256
+    # one fp32 per query row (D = rowsum(dO * O)), plus, for this small grid
+    # (2 * 2 * 32 = 128 dK/dV workgroups at N = 4096), fp32 partial dK/dV of the
+    # whole group of 4 query heads split 4 ways (128 * 2 < 1024), plus alignment
+    assert f(4096) == 2 * 8 * 4096 * 4 + 4 * 2 * 2 * 4096 * 2 * 128 * 4
+    # MHA, d = 256, or a grid of >= 512 dK/dV workgroups: D only
+    assert lib.attn_bwd_workspace_bytes(2, 4096, 8, 8, 128) == 2 * 8 * 4096 * 4
+    assert lib.attn_bwd_workspace_bytes(2, 4096, 8, 2, 256) == 2 * 8 * 4096 * 4
+    assert lib.attn_bwd_workspace_bytes(4, 16384, 8, 2, 128) == 4 * 8 * 16384 * 4
+    # MQA, B = 4, N = 4096, Hq = 32: 128 workgroups, split 8 ways (the smallest divisor reaching 1024)
+    assert lib.attn_bwd_workspace_bytes(4, 4096, 32, 1, 128) == 4 * 32 * 4096 * 4 + 8 * 2 * 4 * 4096 * 128 * 4
     assert lib.attn_bwd_workspace_bytes(0, 16, 1, 1, 64) == 0
     assert lib.attn_bwd_workspace_bytes(1, 16, 3, 2, 64) == 0
 

@@ -95,8 +95,23 @@ def test_full_mask_equals_dense_bitwise(gpu_device, n, d, causal):
     log(f"all-ones mask n{n} d{d} causal={causal}")
     a = run_fwd_bwd(x, "bf16", causal, 1.0 / np.sqrt(d), gpu_device, block_mask=ones)
     b = run_fwd_bwd(x, "bf16", causal, 1.0 / np.sqrt(d), gpu_device)
-    for u, w in zip(a, b):
-        assert np.array_equal(u, w)
+    # This small GQA grid (B * Hkv * ceil(N / 128) < 512 dK/dV workgroups, d <= 128)
+    # makes the dense pass split each group's two query heads over two workgroups
+    # and sum their fp32 partial dK/dV afterwards (include/attn.h,
+    # attn_bwd_workspace_bytes); the block-sparse pass sums both heads in one
+    # workgroup.  Those dK/dV differ only in the fp32 summation order: one bf16
+    # rounding of the element, or, where the sum cancels to near zero, the fp32
+    # reordering error of its terms (bounded here by 1e-4 of the largest element,
+    # 200x below the stated 2e-2 tolerance); everything else is bitwise equal.
+    split = d <= 128
+    for name, u, w in zip(("o", "lse", "dq", "dk", "dv"), a, b):
+        if split and name in ("dk", "dv"):
+            diff = np.abs(u - w)
+            i = np.unravel_index(np.argmax(diff), diff.shape)
+            log(f"  {name}: max |sparse - dense| {diff[i]:.3e} at |dense| {abs(w[i]):.3e}")
+            assert np.all(diff <= 2.0 ** -7 * np.abs(w) + 1e-4 * np.abs(w).max()), name
+        else:
+            assert np.array_equal(u, w), name
 
 
 def test_lower_block_triangle_is_causal_bitwise(gpu_device):
