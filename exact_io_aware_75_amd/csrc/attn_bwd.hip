@@ -282,10 +282,19 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   // (d = 256 never splits: its registers are already full)
   const int hs = D <= 128 ? a.hsplit : 1;
   const int nkb = (a.Nk + KV_BN - 1) / KV_BN;
-  const int total = nkb * a.Hkv * a.B * hs;
-  const int Lw = xcd_remap(blockIdx.x, total);
-  const int bgs = Lw / nkb;
-  const int kb = Lw - bgs * nkb;
+  int bgs, kb;
+  if constexpr (CAUSAL && !SPARSE) {
+    // Causal key blocks differ in work (the first sees every query):
+    // weight-major order with consecutive work items on consecutive XCDs,
+    // as in the causal forward pass.
+    const int G = a.Hkv * a.B * hs;
+    kb = blockIdx.x / G;
+    bgs = blockIdx.x - kb * G;
+  } else {
+    const int Lw = xcd_remap(blockIdx.x, nkb * a.Hkv * a.B * hs);
+    bgs = Lw / nkb;
+    kb = Lw - bgs * nkb;
+  }
   const int bg = bgs / hs;
   const int split = bgs - bg * hs;
   const int gs = a.group / hs;  // query heads of the group this workgroup covers
@@ -593,10 +602,19 @@ attn_bwd_dq_kernel(BwdArgs a) {
 
   // ---- which (batch, head, row block) this workgroup owns; heaviest first ----
   const int nblk = (a.N + DQ_BM - 1) / DQ_BM;
-  const int total = nblk * a.Hq * a.B;
-  const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / nblk;
-  const int rb = nblk - 1 - (L - bh * nblk);
+  int bh, rb;
+  if constexpr (CAUSAL && !SPARSE) {
+    // weight-major, consecutive work items on consecutive XCDs (as in the
+    // causal forward pass)
+    const int BH = a.Hq * a.B;
+    const int r = blockIdx.x / BH;
+    bh = blockIdx.x - r * BH;
+    rb = nblk - 1 - r;
+  } else {
+    const int L = xcd_remap(blockIdx.x, nblk * a.Hq * a.B);
+    bh = L / nblk;
+    rb = nblk - 1 - (L - bh * nblk);
+  }
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
   const int g = h / a.group;

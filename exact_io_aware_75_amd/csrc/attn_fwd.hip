@@ -153,10 +153,23 @@ attn_fwd_kernel(FwdArgs a) {
 
   // ---- which (batch, head, row block) this workgroup owns ----
   const int nblk = (a.N + FWD_BM - 1) / FWD_BM;
-  const int total = nblk * a.Hq * a.B;
-  const int L = xcd_remap(blockIdx.x, total);
-  const int bh = L / nblk;
-  const int rb = nblk - 1 - (L - bh * nblk);  // heaviest (causal) row blocks first
+  int bh, rb;
+  if constexpr (CAUSAL && !SPARSE) {
+    // Causal row blocks differ in work.  Weight-major order: the heaviest
+    // row block of every (batch, head) first, then the next heaviest, ...
+    // Consecutive work items go to consecutive XCDs (the hardware's round
+    // robin), so every XCD gets an equal share of each weight and, when
+    // B * Hq is a multiple of 8, every row block of a fixed set of heads
+    // (their K/V stays in that XCD's L2).
+    const int BH = a.Hq * a.B;
+    const int r = blockIdx.x / BH;
+    bh = blockIdx.x - r * BH;
+    rb = nblk - 1 - r;
+  } else {
+    const int L = xcd_remap(blockIdx.x, nblk * a.Hq * a.B);
+    bh = L / nblk;
+    rb = nblk - 1 - (L - bh * nblk);
+  }
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
   const int g = h / a.group;
