@@ -24,9 +24,13 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 int check_shape(int B, int N, int Hq, int Hkv, int d) {
   if (B < 1 || N < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return ATTN_ERR_SHAPE;
   if (d != 64 && d != 128 && d != 256) return ATTN_ERR_HEADDIM;
-  // element offsets inside one (batch, head) slice and the row-block grid stay in int range
-  if ((long long)N * Hq * d >= (1LL << 31) || (long long)B * Hq * ((N + 127) / 128) >= (1LL << 31))
-    return ATTN_ERR_TOO_LARGE;
+  // Element offsets inside one (batch, head) slice and the row-block grid stay
+  // in int range.  Each product is formed only once its factors are known to
+  // keep it below 2^63 (all sizes are positive ints here).
+  const long long nh = (long long)N * Hq;   // < 2^62
+  if (nh >= (1LL << 31) / d) return ATTN_ERR_TOO_LARGE;  // N * Hq * d >= 2^31 (d divides 2^31)
+  const long long bh = (long long)B * Hq;   // < 2^62
+  if (bh >= (1LL << 31) || bh * ((N - 1) / 128 + 1) >= (1LL << 31)) return ATTN_ERR_TOO_LARGE;
   return ATTN_OK;
 }
 
@@ -179,9 +183,7 @@ int attn_fwd_rect(const void* q, const void* k, const void* v, void* o, float* l
 }
 
 size_t attn_fwd_splitkv_workspace_bytes(int B, int Nq, int Hq, int d, int num_splits) {
-  if (B < 1 || Nq < 1 || Hq < 1 || (d != 64 && d != 128 && d != 256) || num_splits < 1 ||
-      num_splits > ATTN_MAX_SPLITS)
-    return 0;
+  if (check_shape(B, Nq, Hq, 1, d) != ATTN_OK || num_splits < 1 || num_splits > ATTN_MAX_SPLITS) return 0;
   return attn::split_workspace_layout(B, Nq, Hq, d, num_splits).total;
 }
 
@@ -341,7 +343,8 @@ namespace {
 // Launch limits of the standard path: one row workgroup per (batch, head,
 // query row) in grid x, one (batch, head) per grid z of the tile products.
 int check_std_grid(int B, int N, int Hq) {
-  if ((long long)B * Hq * N >= (1LL << 24) || (long long)B * Hq > 65535) return ATTN_ERR_TOO_LARGE;
+  const long long bh = (long long)B * Hq;  // < 2^62; then bh * N < 2^24 * 2^31
+  if (bh > 65535 || bh * N >= (1LL << 24)) return ATTN_ERR_TOO_LARGE;
   return ATTN_OK;
 }
 
