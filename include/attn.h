@@ -240,9 +240,11 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
  * Standard (materialising) attention: the baseline the pages measure the
  * IO-aware method against (FlashAttention-1 news page, "FlashAttention"
  * section: standard attention writes the N x N attention matrix to HBM and
- * reads it back; FlashAttention-2 review, "Введение").  Same result and the
- * same arguments, layouts and error behaviour as attn_fwd / attn_bwd, but
- * every intermediate goes through device memory, in separate launches:
+ * reads it back; FlashAttention-2 review, "Введение").  Same result, tensor
+ * layouts, dtypes, scale and causal semantics and error behaviour as
+ * attn_fwd / attn_bwd (attn_bwd_standard takes no o or lse: it reads the
+ * stored P instead), but every intermediate goes through device memory, in
+ * separate launches:
  *
  *   attn_fwd_standard   S = scale q k^T  (float32, full N x N per head)
  *                       P = softmax(S) row-wise with the causal mask applied
