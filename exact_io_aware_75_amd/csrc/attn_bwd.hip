@@ -608,7 +608,8 @@ attn_bwd_dq_kernel(BwdArgs a) {
     // causal forward pass)
     const int BH = a.Hq * a.B;
     const int r = blockIdx.x / BH;
-    bh = blockIdx.x - r * BH;
+    const int i = blockIdx.x - r * BH;
+    bh = (BH & 7) == 0 ? (i & 7) * (BH >> 3) + (i >> 3) : i;  // contiguous heads per XCD
     rb = nblk - 1 - r;
   } else {
     const int L = xcd_remap(blockIdx.x, nblk * a.Hq * a.B);

@@ -159,11 +159,15 @@ attn_fwd_kernel(FwdArgs a) {
     // row block of every (batch, head) first, then the next heaviest, ...
     // Consecutive work items go to consecutive XCDs (the hardware's round
     // robin), so every XCD gets an equal share of each weight and, when
-    // B * Hq is a multiple of 8, every row block of a fixed set of heads
-    // (their K/V stays in that XCD's L2).
+    // B * Hq is a multiple of 8, every row block of a fixed set of heads.
+    // Within a weight class the XCD of item i is i % 8 (B * Hq a multiple of
+    // 8); XCD x takes the contiguous range of (batch, head) pairs
+    // [x B Hq / 8, (x + 1) B Hq / 8), so the query heads of a GQA group and
+    // the heads of one batch share K/V in one L2.
     const int BH = a.Hq * a.B;
     const int r = blockIdx.x / BH;
-    bh = blockIdx.x - r * BH;
+    const int i = blockIdx.x - r * BH;
+    bh = (BH & 7) == 0 ? (i & 7) * (BH >> 3) + (i >> 3) : i;
     rb = nblk - 1 - r;
   } else {
     const int L = xcd_remap(blockIdx.x, nblk * a.Hq * a.B);
