@@ -6,6 +6,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 
 #include "../../include/attn.h"
@@ -58,6 +59,32 @@ int check_device() {
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// ATTN_DEBUG=1 in the environment (read once per process): every call waits
+// for its stream and reports an execution error of its kernels as
+// ATTN_ERR_HIP, instead of leaving it to a later call.  For debugging only:
+// it serialises the caller's stream.
+bool debug_sync() {
+  static const bool on = [] {
+    const char* v = std::getenv("ATTN_DEBUG");
+    return v != nullptr && v[0] != '\0' && std::strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+// Result of a call's launches: a launch error, or under ATTN_DEBUG an
+// execution error found by synchronising the stream.
+int finish(hipError_t e, void* stream) {
+  if (e == hipSuccess && debug_sync()) {
+    e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e == hipSuccess) e = hipGetLastError();
+  }
+  if (e != hipSuccess) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_HIP;
+  }
+  return ATTN_OK;
+}
 
 // Block-mask arguments of the block-sparse entry points.
 int check_mask(const unsigned char* block_mask, int mask_heads, int N, int Hkv, attn::SparseArgs* sp) {
@@ -157,13 +184,8 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
     a.opart = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.opart_off);
     a.lsepart = reinterpret_cast<float*>(static_cast<char*>(workspace) + w.lsepart_off);
   }
-  hipError_t e = attn::launch_fwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0,
-                                  static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
-    return ATTN_ERR_HIP;
-  }
-  return ATTN_OK;
+  return finish(attn::launch_fwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0, static_cast<hipStream_t>(stream)),
+                stream);
 }
 
 }  // namespace
@@ -272,13 +294,9 @@ int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, int 
   a.coff = clamp_offset(causal_offset, N, Nk);
   a.hsplit = ws.hsplit;
   a.dkv_part = ws.hsplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_off) : nullptr;
-  hipError_t e = attn::launch_bwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0, stages,
-                                  static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
-    return ATTN_ERR_HIP;
-  }
-  return ATTN_OK;
+  return finish(attn::launch_bwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0, stages,
+                                 static_cast<hipStream_t>(stream)),
+                stream);
 }
 
 }  // namespace
@@ -392,13 +410,9 @@ int std_common(bool fwd, const void* q, const void* k, const void* v, const void
   a.causal = causal != 0;
   a.scale = scale;
   const bool bf16 = dtype == ATTN_DTYPE_BF16;
-  hipError_t e = fwd ? attn::launch_std_fwd(a, bf16, static_cast<hipStream_t>(stream))
-                     : attn::launch_std_bwd(a, bf16, static_cast<hipStream_t>(stream));
-  if (e != hipSuccess) {
-    g_last_hip_error = (int)e;
-    return ATTN_ERR_HIP;
-  }
-  return ATTN_OK;
+  return finish(fwd ? attn::launch_std_fwd(a, bf16, static_cast<hipStream_t>(stream))
+                    : attn::launch_std_bwd(a, bf16, static_cast<hipStream_t>(stream)),
+                stream);
 }
 
 }  // namespace

@@ -39,7 +39,10 @@
  * Errors.  Each entry point returns an attn_status_t.  Arguments are
  * validated before anything is launched; on any error nothing is written.
  * A failed launch returns ATTN_ERR_HIP and attn_last_hip_error() gives the
- * hipError_t of the failing call on this thread.
+ * hipError_t of the failing call on this thread.  With the environment
+ * variable ATTN_DEBUG set (to anything but "" or "0") when the library first
+ * checks it, every call also waits for its stream and returns ATTN_ERR_HIP if
+ * its kernels failed: a debugging aid that makes calls synchronous.
  */
 #ifndef ATTN_H_
 #define ATTN_H_
