@@ -22,3 +22,17 @@ def test_excess_accepts_rounding_and_rejects_more():
     assert excess(rounded, ref, 0.0, "bf16") <= 0
     assert excess(rounded + 0.03, ref, 0.0, "bf16") > 0
     assert excess(ref + 0.019, ref, 0.02, "bf16") <= 0
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU: --gpus N > 1 exits with a message saying so
+    (before anything touches a GPU)."""
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and "--gpus 2" in r.stderr
