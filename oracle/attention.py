@@ -50,7 +50,7 @@ no allowed key.  Each device's partial results for one query shard combine
 exactly through their LSEs: LSE = ln sum_p exp(LSE_p) and
 O = sum_p exp(LSE_p - LSE) O_p.
 
-Readings where the pages are silent (listed again in the design doc):
+Readings where the pages are silent:
   * causal orientation: query i may attend key j iff j <= i (the pages only
     say the masked triangle is skipped rather than computed and zeroed;
     FlashAttention-2 review, "Алгоритм вычисления" subsection);
