@@ -743,7 +743,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
-              "(the kernels shard trivially over batch and heads, but this build measures one GPU).",
+              "(the kernels shard trivially over batch and heads; this benchmark measures one GPU).",
               file=sys.stderr)
         sys.exit(2)
     if args.no_cpu_baseline:
