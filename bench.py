@@ -36,7 +36,9 @@ Prints one JSON line.  Besides the throughput it carries
   standard      standard attention (attn_fwd_standard / attn_bwd_standard),
                 which writes the N x N scores and probabilities to HBM, against
                 the tiled kernels on the step's shape: times, speed-ups, extra
-                device memory and algorithmic HBM bytes of each.
+                device memory and algorithmic HBM bytes of each; `by_N`: the
+                speed-ups over the hidden-2048, d = 128 sequence-length sweep
+                (B * N = 16384).
 --sweep also prints per-workload forward/backward TFLOP/s for every full-size
 configuration to stderr.
 """
@@ -455,6 +457,31 @@ def standard_measure():
             "standard_bwd_hbm_GBps": round(hb["standard_bwd"] / (t_sb / 1e3) / 1e9, 1)}
     del q, k, v, do, o, lse, dq, dk, dv, ws_s, ws_t
     torch.cuda.empty_cache()
+    # the same comparison over the sequence lengths of the hidden-2048, d = 128
+    # sweep (B * N = 16384 tokens, H = 16), median of 5 launches each
+    out["by_N"] = []
+    for n2 in (1024, 2048, 8192, 16384):
+        b2 = 16384 // n2
+        q, k, v, do = (mk_shape(g, dev, b2, n2, h, d) for _ in range(4))
+        o, lse = torch.empty_like(q), torch.empty((b2, h, n2), dtype=torch.float32, device=dev)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        sw = ea.attn_standard_workspace_bytes(b2, n2, h, h, d)
+        ws_s = torch.empty(sw, dtype=torch.uint8, device=dev)
+        ws_t = torch.empty(ea.attn_bwd_workspace_bytes(b2, n2, h, h, d), dtype=torch.uint8, device=dev)
+        row = {"N": n2, "B": b2, "standard_workspace_GB": round(sw / 1e9, 2)}
+        for causal in (False, True):
+            t_sf = _median_ms(lambda: ea.attn_fwd_standard(q, k, v, o, lse, ws_s, causal, sc, stream), stream, reps=5)
+            t_sb = _median_ms(lambda: ea.attn_bwd_standard(q, k, v, do, dq, dk, dv, ws_s, causal, sc, stream), stream,
+                              reps=5)
+            t_tf = _median_ms(lambda: ea.attn_fwd(q, k, v, o, lse, causal, sc, stream), stream, reps=5)
+            t_tb = _median_ms(lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws_t, causal, sc, stream), stream,
+                              reps=5)
+            row["causal" if causal else "noncausal"] = {
+                "speedup_fwd": round(t_sf / t_tf, 2), "speedup_bwd": round(t_sb / t_tb, 2),
+                "speedup_fwd_bwd": round((t_sf + t_sb) / (t_tf + t_tb), 2)}
+        out["by_N"].append(row)
+        del q, k, v, do, o, lse, dq, dk, dv, ws_s, ws_t
+        torch.cuda.empty_cache()
     return out
 
 
