@@ -30,6 +30,8 @@ Prints one JSON line.  Besides the throughput it carries
                 split-KV forward (attn_fwd_splitkv) on a short-query shape,
                 128 queries against 65536 keys, B = 1, H = 32, d = 128,
                 against the unsplit kernel;
+  secondary_ceilings  exponential and LDS-read throughput measured by
+                libattn_probe.so, beside what the non-causal forward needs;
   mfma_ceiling  the sustained MFMA rate measured on this part by
                 libattn_probe.so (random and constant bf16 operands); the
                 roofline entry also gives the dominant kernel's fraction of it;
@@ -236,6 +238,7 @@ def run(args):
         line["standard"] = standard_measure()
     ceil = mfma_ceiling()
     line["mfma_ceiling"] = ceil
+    line["secondary_ceilings"] = secondary_ceilings(fwd_tf[False], d)
     roofline["frac_of_measured_ceiling"] = round(achieved / ceil["random_bf16_tflops"], 4)
     if args.sweep:
         sweep()
@@ -526,6 +529,64 @@ def mfma_ceiling():
     return {"what": "v_mfma_f32_32x32x16_bf16 back to back, 2 wavefronts per SIMD on all 256 CUs",
             "random_bf16_tflops": round(res["random"], 1), "constant_tflops": round(res["constant"], 1),
             "frac_of_spec_random": round(res["random"] / PEAK_BF16_TFLOPS, 4)}
+
+
+def secondary_ceilings(fwd_tflops, d):
+    """Exponential and LDS-read throughput of this part (libattn_probe.so),
+    beside what the non-causal forward at `fwd_tflops` needs: one exponential
+    per score (FLOPs / 4d) and, per wavefront and 32 MFMAs (2^20 FLOP), 16 KiB
+    of K and 16 KiB of V^T read from LDS (0.03125 B/FLOP at d = 128)."""
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "exact_io_aware_75_amd", "libattn_probe.so"))
+    vp, i = ctypes.c_void_p, ctypes.c_int
+    lib.attn_probe_exp.argtypes = [vp, vp, i, i, vp]
+    lib.attn_probe_lds.argtypes = [vp, vp, i, i, vp]
+    lib.attn_probe_exp.restype = lib.attn_probe_lds.restype = i
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    out = {}
+    wgs, iters = 256 * 8, 20000
+    seed = torch.rand(wgs * 256 * 8, device=dev)
+    res = torch.empty(wgs * 256, device=dev)
+
+    def run_exp():
+        if lib.attn_probe_exp(ctypes.c_void_p(seed.data_ptr()), ctypes.c_void_p(res.data_ptr()), wgs, iters, sp) != 0:
+            raise RuntimeError("attn_probe_exp failed")
+
+    t = _median_ms(run_exp, stream, reps=5)
+    exp_rate = wgs * 256.0 * iters * 8 / (t / 1e3)
+    need = fwd_tflops * 1e12 / (4 * d)
+    out["exp"] = {"what": "v_exp_f32, 8 independent chains per lane, 8 workgroups of 4 wavefronts per CU",
+                  "measured_per_s": float(f"{exp_rate:.4g}"), "forward_needs_per_s": float(f"{need:.4g}"),
+                  "fraction_used": round(need / exp_rate, 3)}
+    wgs, iters = 256 * 4, 20000
+    res = torch.empty(wgs * 256, device=dev)
+    clk = torch.zeros(2, dtype=torch.int64, device=dev)
+
+    def run_lds():
+        if lib.attn_probe_lds(ctypes.c_void_p(res.data_ptr()), ctypes.c_void_p(clk.data_ptr()), wgs, iters, sp) != 0:
+            raise RuntimeError("attn_probe_lds failed")
+
+    t = _median_ms(run_lds, stream, reps=5)
+    lds_bps = wgs * 256.0 * iters * 8 * 16 / (t / 1e3)
+    c = clk.cpu().numpy().astype(np.float64)
+    ghz = c[0] / c[1] * 0.1 if c[1] > 0 else float("nan")  # shader cycles per 10 ns tick
+    # 32 KiB per 32 MFMAs of 32 x 32 x 16 (2 FLOP per multiply-add): 2^15 B / 2^20 FLOP
+    need_lds = fwd_tflops * 1e12 * (32768.0 / (32 * 32 * 32 * 16 * 2)) if d == 128 else float("nan")
+    out["lds"] = {"what": "ds_read_b128, conflict-free, 4 workgroups of 4 wavefronts per CU",
+                  "measured_TBps": round(lds_bps / 1e12, 1),
+                  "per_CU_bytes_per_clock": round(lds_bps / 256 / (ghz * 1e9), 1),
+                  "probe_clock_GHz": round(ghz, 2),
+                  "forward_needs_TBps": round(need_lds / 1e12, 1),
+                  "fraction_used": round(need_lds / lds_bps, 3)}
+    del seed, res, clk
+    torch.cuda.empty_cache()
+    return out
 
 
 def mk_shape(g, dev, b, n, h, d):

@@ -1,7 +1,8 @@
 /*
- * attn_probe.h -- C ABI of libattn_probe.so, the MFMA throughput probe that
- * the benchmark uses as the measured ceiling for the attention kernels'
- * matrix work on MI355X (gfx950).  Not part of the attention library.
+ * attn_probe.h -- C ABI of libattn_probe.so, the throughput probes the
+ * benchmark uses as measured ceilings for the attention kernels' matrix
+ * work (MFMA), exponentials and LDS reads on MI355X (gfx950).  Not part of
+ * the attention library.
  *
  * The dense bf16 peak in AMD's specification (2516.6 TFLOP/s = 256 CUs x
  * 4096 FLOP/clock x 2.4 GHz) assumes the full shader clock.  Under sustained
@@ -33,6 +34,24 @@ int attn_probe_mfma(const void* operands, float* out, int workgroups, int iters,
 
 /* Matrix FLOPs one attn_probe_mfma call performs (2 per multiply-add). */
 double attn_probe_mfma_flops(int workgroups, int iters);
+
+/*
+ * v_exp_f32 throughput: `workgroups` x 256 threads each run `iters` x 8
+ * exponentials (eight independent chains).  in: workgroups * 256 * 8 floats
+ * (seed values), out: workgroups * 256 floats (results, only to keep the work
+ * live); device memory, 4-byte aligned.  Status codes as attn_probe_mfma.
+ */
+int attn_probe_exp(const float* in, float* out, int workgroups, int iters, void* stream);
+
+/*
+ * LDS read bandwidth: `workgroups` x 256 threads each read `iters` x 8 x 16
+ * bytes from LDS with conflict-free ds_read_b128.  out: workgroups * 256
+ * floats (results, only to keep the work live); clk: 2 values written by
+ * workgroup 0, the shader-clock and the 100 MHz real-time counter deltas over
+ * its loop (their ratio times 100 MHz is the shader clock).  Device memory;
+ * status codes as attn_probe_mfma.
+ */
+int attn_probe_lds(float* out, unsigned long long* clk, int workgroups, int iters, void* stream);
 
 #ifdef __cplusplus
 }

@@ -243,7 +243,7 @@ def test_probe_library_exports_its_header():
         build()
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "attn_probe.h")).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b(attn_[a-z0-9_]+)\s*\(", text)))
-    assert names == ["attn_probe_mfma", "attn_probe_mfma_flops"]
+    assert names == ["attn_probe_exp", "attn_probe_lds", "attn_probe_mfma", "attn_probe_mfma_flops"]
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True).stdout
     for name in names:
         assert re.search(rf"\bT {name}\b", out), name
@@ -252,3 +252,12 @@ def test_probe_library_exports_its_header():
     assert lib.attn_probe_mfma_flops(2, 3) == 2 * 4 * 3 * 16 * 2 * 32 * 32 * 16
     assert lib.attn_probe_mfma(None, ctypes.c_void_p(A), 1, 1, None) == 1
     assert lib.attn_probe_mfma(ctypes.c_void_p(A), ctypes.c_void_p(A), 0, 1, None) == 2
+
+
+def test_probe_library_rejects_bad_arguments_of_every_probe():
+    path = os.path.join(ROOT, "exact_io_aware_75_amd", "libattn_probe.so")
+    lib = ctypes.CDLL(path)
+    assert lib.attn_probe_exp(None, ctypes.c_void_p(A), 1, 1, None) == 1
+    assert lib.attn_probe_exp(ctypes.c_void_p(A), ctypes.c_void_p(A), 1, 0, None) == 2
+    assert lib.attn_probe_lds(ctypes.c_void_p(A), None, 1, 1, None) == 1
+    assert lib.attn_probe_lds(ctypes.c_void_p(A), ctypes.c_void_p(A), (1 << 20) + 1, 1, None) == 2
