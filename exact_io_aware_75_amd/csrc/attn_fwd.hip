@@ -40,8 +40,10 @@
 //    exponentiates the first half of its probabilities; the second half is
 //    exponentiated under the first half of tile j's P V products.  A single
 //    wavefront's VALU work thus issues in the shadow of its own MFMAs instead
-//    of waiting for the other wavefront on the SIMD.  The key tiles after the
-//    last unmasked one (the diagonal and the ragged end) run unpipelined.
+//    of waiting for the other wavefront on the SIMD.  Non-causal, the tiles
+//    after the last unmasked one (the ragged end) run unpipelined; causal at
+//    d >= 128, the masked tiles are pipelined too and only each wavefront's
+//    last tile is not (at d = 64 the masked tiles run unpipelined).
 //  * K/V tiles go HBM -> LDS by buffer_load_dwordx4 ... lds (no register
 //    staging) through a buffer resource whose record count ends at the last
 //    key: rows past the end of the sequence arrive as zeros, with no clamp
@@ -540,8 +542,32 @@ attn_fwd_kernel(FwdArgs a) {
     step(j + 1, kb0, vb1, sB, sA, std::false_type{}, std::true_type{});
     iter_end();
   }
+  if constexpr (CAUSAL && D >= 128) {
+    // the tiles up to this wavefront's last one (the diagonal and the ragged
+    // end among them), pipelined like the steady state with the element mask
+    // on; j is even here, so the buffers alternate as above.  (At d = 64 the
+    // extra tile bodies spill registers.)
+    for (; j + 2 < nwave; j += 2) {
+      iter_loads(j, kb0, vb1);
+      step(j, kb1, vb0, sA, sB, std::true_type{}, std::true_type{});
+      iter_end();
+      iter_loads(j + 1, kb1, vb0);
+      step(j + 1, kb0, vb1, sB, sA, std::true_type{}, std::true_type{});
+      iter_end();
+    }
+    if (j + 1 < nwave) {  // two tiles left: the first pipelined, the last's scores in sB
+      iter_loads(j, kb0, vb1);
+      step(j, kb1, vb0, sA, sB, std::true_type{}, std::true_type{});
+      iter_end();
+      iter_loads(j + 1, kb1, vb0);
+      step(j + 1, kb0, vb1, sB, sA, std::true_type{}, std::false_type{});
+      iter_end();
+      j += 2;
+    }
+  }
   // remaining tiles: the diagonal / ragged ones, the last unmasked ones, and
-  // tiles only other wavefronts need.  Not overlapped: the next tile's scores
+  // tiles only other wavefronts need (causal at d >= 128: only this
+  // wavefront's last tile, if any, is computed here).  Not overlapped: the next tile's scores
   // are formed after this one's P V, in the same registers.
   for (; j < ntiles; ++j) {
     uint16_t* kcur = (j & 1) ? kb1 : kb0;   // K buffer j & 1 receives K_{j+2}
