@@ -41,9 +41,9 @@
 //    exponentiated under the first half of tile j's P V products.  A single
 //    wavefront's VALU work thus issues in the shadow of its own MFMAs instead
 //    of waiting for the other wavefront on the SIMD.  Non-causal, the tiles
-//    after the last unmasked one (the ragged end) run unpipelined; causal at
-//    d >= 128, the masked tiles are pipelined too and only each wavefront's
-//    last tile is not (at d = 64 the masked tiles run unpipelined).
+//    after the last unmasked one (the ragged end) run unpipelined; causal,
+//    the masked tiles (the diagonal) are pipelined too and only each
+//    wavefront's last tile is not.
 //  * K/V tiles go HBM -> LDS by buffer_load_dwordx4 ... lds (no register
 //    staging) through a buffer resource whose record count ends at the last
 //    key: rows past the end of the sequence arrive as zeros, with no clamp
@@ -533,8 +533,15 @@ attn_fwd_kernel(FwdArgs a) {
     __syncthreads();
   };
   int j = 0;
-  // steady state: tile j unmasked and tile j + 1 computed by this wavefront
-  for (; j + 2 < nfull; j += 2) {
+  // steady state: tiles j and j + 1 unmasked, tile j + 2 computed by this
+  // wavefront (its scores are formed here, its mask applied when its turn
+  // comes) and, except causal at d = 64, unmasked too.  At d = 64 a causal
+  // wavefront's only masked tile is its last, so the loop runs up to it and
+  // the two-tile block below takes the rest.  (Where that does not pay -- d >=
+  // 128, which has its own masked loop, and split-KV -- the stricter bound
+  // keeps the kernels free of register spills.)
+  constexpr bool UP_TO_LAST = CAUSAL && D == 64 && !SPLIT;
+  for (; UP_TO_LAST ? (j + 2 <= nfull && j + 2 < nwave) : (j + 2 < nfull); j += 2) {
     iter_loads(j, kb0, vb1);
     step(j, kb1, vb0, sA, sB, std::false_type{}, std::true_type{});
     iter_end();
@@ -542,20 +549,25 @@ attn_fwd_kernel(FwdArgs a) {
     step(j + 1, kb0, vb1, sB, sA, std::false_type{}, std::true_type{});
     iter_end();
   }
-  if constexpr (CAUSAL && D >= 128) {
+  if constexpr (CAUSAL && (D >= 128 || UP_TO_LAST)) {
     // the tiles up to this wavefront's last one (the diagonal and the ragged
     // end among them), pipelined like the steady state with the element mask
-    // on; j is even here, so the buffers alternate as above.  (At d = 64 the
-    // extra tile bodies spill registers.)
-    for (; j + 2 < nwave; j += 2) {
-      iter_loads(j, kb0, vb1);
-      step(j, kb1, vb0, sA, sB, std::true_type{}, std::true_type{});
-      iter_end();
-      iter_loads(j + 1, kb1, vb0);
-      step(j + 1, kb0, vb1, sB, sA, std::true_type{}, std::true_type{});
-      iter_end();
+    // on; j is even here, so the buffers alternate as above.  At d = 64 (one
+    // masked 128-key tile per wavefront) only the last two tiles take this
+    // path: a second pair of masked tile bodies spills registers there.
+    if constexpr (D >= 128) {
+      for (; j + 2 < nwave; j += 2) {
+        iter_loads(j, kb0, vb1);
+        step(j, kb1, vb0, sA, sB, std::true_type{}, std::true_type{});
+        iter_end();
+        iter_loads(j + 1, kb1, vb0);
+        step(j + 1, kb0, vb1, sB, sA, std::true_type{}, std::true_type{});
+        iter_end();
+      }
     }
-    if (j + 1 < nwave) {  // two tiles left: the first pipelined, the last's scores in sB
+    // two tiles left (at d >= 128 the loop above leaves at most two): the
+    // first pipelined, the last's scores in sB
+    if (D >= 128 ? j + 1 < nwave : j + 2 == nwave) {
       iter_loads(j, kb0, vb1);
       step(j, kb1, vb0, sA, sB, std::true_type{}, std::true_type{});
       iter_end();
@@ -566,9 +578,11 @@ attn_fwd_kernel(FwdArgs a) {
     }
   }
   // remaining tiles: the diagonal / ragged ones, the last unmasked ones, and
-  // tiles only other wavefronts need (causal at d >= 128: only this
-  // wavefront's last tile, if any, is computed here).  Not overlapped: the next tile's scores
-  // are formed after this one's P V, in the same registers.
+  // tiles only other wavefronts need (causal: at most this wavefront's last
+  // tile is computed here, except at d = 64 when a causal offset leaves more
+  // than two tiles after the unmasked ones, and for causal split-KV at
+  // d = 64).  Not overlapped: the next tile's scores are formed after
+  // this one's P V, in the same registers.
   for (; j < ntiles; ++j) {
     uint16_t* kcur = (j & 1) ? kb1 : kb0;   // K buffer j & 1 receives K_{j+2}
     uint16_t* knext = (j & 1) ? kb0 : kb1;

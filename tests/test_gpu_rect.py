@@ -53,6 +53,13 @@ SMALL = [
     (1, 500, 200, 4, 1, 128, "bf16", True, 1000),    # past the last key: every key visible
     (1, 300, 300, 2, 2, 64, "bf16", True, -10000),   # before the first key: no row sees a key
     (1, 520, 1300, 8, 2, 256, "fp16", True, None),
+    # diagonals at unaligned offsets over many key tiles: a wavefront's rows
+    # can cross two masked tiles, with 0, 1 or 2 unmasked tiles between the
+    # paired steady-state steps and its last tile
+    (1, 400, 1100, 2, 2, 64, "bf16", True, 333),
+    (2, 700, 900, 4, 2, 64, "fp16", True, 40),
+    (1, 450, 1000, 2, 2, 128, "bf16", True, 211),
+    (1, 260, 2000, 2, 1, 128, "fp16", True, 1650),
 ]
 
 
