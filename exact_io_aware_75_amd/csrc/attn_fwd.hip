@@ -6,9 +6,9 @@
 //    result is folded into the output (FlashAttention-2 announcement, "具体实现"
 //    section; FlashAttention-1 news page, "FlashAttention" section).
 //  * Parallel over sequence length: one workgroup per (batch, query head,
-//    block of 256 query rows, 128 when causal or at d = 256), so the grid
-//    fills 256 CUs even for small batch * heads (announcement, "具体实现";
-//    review, "Параллелизм").
+//    block of 256 query rows, 128 when causal, at d = 256 or over short key
+//    sequences), so the grid fills 256 CUs even for small batch * heads
+//    (announcement, "具体实现"; review, "Параллелизм").
 //  * Work split inside a workgroup: each 64-lane wavefront owns 32 query rows
 //    and all wavefronts share the K/V tiles, so wavefronts never exchange
 //    partial outputs (announcement, "具体实现": Q split across warps, K/V
@@ -28,7 +28,8 @@
 //  * Occupancy: two wavefronts per SIMD (<= 256 registers each) at d <= 128:
 //    one workgroup of eight wavefronts per CU when non-causal, so a K/V tile
 //    staged in LDS serves 256 query rows, or two workgroups of four when
-//    causal.  At d = 256 one wavefront per SIMD.
+//    causal or when the key sequence is short.  At d = 256 one wavefront per
+//    SIMD.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 //    accumulator holds one query per lane and 16 keys per register block, so
 //    the row max / row sum are in-lane except one v_permlane32_swap between
@@ -62,17 +63,25 @@ namespace {
 
 // Wavefronts per workgroup (32 query rows each).  Non-causal at d <= 128:
 // eight, one workgroup per CU at two wavefronts per SIMD, so each K/V tile is
-// staged once per 256 query rows.  Causal: four, since the wavefronts of a
+// staged once per 256 query rows -- except over short key sequences (NARROW;
+// the host picks it below NarrowKeys), where each workgroup's loop is short
+// next to its fixed prologue and epilogue: there two workgroups of four per
+// CU, one in its loop while the other loads or stores, win over staging each
+// tile for more rows.  Causal: four, since the wavefronts of a
 // diagonal block have unequal trip counts and wait for the longest at every
 // barrier.  d = 256: four (one wavefront per SIMD).  Block-sparse: four, so
 // that a workgroup's 128 rows are one row of the block mask.  Split-KV: four,
 // since it serves short query sequences, where 256-row blocks would be
 // mostly past the end.
-template <int D, bool CAUSAL, bool SPARSE = false, bool SPLIT = false> struct FwdWG {
-  static constexpr int WAVES = (D <= 128 && !CAUSAL && !SPARSE && !SPLIT) ? 8 : 4;
+template <int D, bool CAUSAL, bool SPARSE = false, bool SPLIT = false, bool NARROW = false> struct FwdWG {
+  static constexpr int WAVES = (D <= 128 && !CAUSAL && !SPARSE && !SPLIT && !NARROW) ? 8 : 4;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BM = WAVES * 32;
 };
+// Key count up to which the non-causal dense forward runs four-wavefront
+// workgroups (the crossover measured on MI355X lies between 2048 and 4096 keys
+// at d = 128, between 8192 and 16384 at d = 64).
+template <int D> struct NarrowKeys { static constexpr int MAX = D == 64 ? 8192 : 2048; };
 constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units: rescale only if the max grows > 2^8
 
 // Key-tile height per head dimension: every K or V tile is 16 KiB.
@@ -96,9 +105,10 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Wavefronts per SIMD the register budget is cut for: two for d <= 128; at
 // d = 256 the resident Q (64 registers) and O^T (128) leave too little for two.
-template <int D, bool CAUSAL, bool SPARSE, bool SPLIT> struct FwdOcc {
+template <int D, bool CAUSAL, bool SPARSE, bool SPLIT, bool NARROW> struct FwdOcc {
   static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1;
-  static constexpr int MIN_WG_PER_CU = WAVES_PER_SIMD * 4 / FwdWG<D, CAUSAL, SPARSE, SPLIT>::WAVES;  // launch-bounds form
+  static constexpr int MIN_WG_PER_CU =
+      WAVES_PER_SIMD * 4 / FwdWG<D, CAUSAL, SPARSE, SPLIT, NARROW>::WAVES;  // launch-bounds form
 };
 
 template <int I, int N, typename F>
@@ -117,14 +127,14 @@ template <int D> struct FwdPrefetch {
   static constexpr int V = 2;
 };
 
-template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT>
-__global__ void __launch_bounds__((FwdWG<D, CAUSAL, SPARSE, SPLIT>::THREADS),
-                                  (FwdOcc<D, CAUSAL, SPARSE, SPLIT>::MIN_WG_PER_CU))
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT, bool NARROW>
+__global__ void __launch_bounds__((FwdWG<D, CAUSAL, SPARSE, SPLIT, NARROW>::THREADS),
+                                  (FwdOcc<D, CAUSAL, SPARSE, SPLIT, NARROW>::MIN_WG_PER_CU))
 attn_fwd_kernel(FwdArgs a) {
   constexpr int BN = FwdTile<D>::BN;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILE = BN * D;          // elements per K or V tile (8192)
-  using WG = FwdWG<D, CAUSAL, SPARSE, SPLIT>;
+  using WG = FwdWG<D, CAUSAL, SPARSE, SPLIT, NARROW>;
   constexpr int FWD_WAVES = WG::WAVES;
   constexpr int FWD_BM = WG::BM;
   constexpr int LPT = TILE / 8 / WG::THREADS;  // 16-byte loads per thread per tensor
@@ -696,9 +706,9 @@ SplitWorkspace split_workspace_layout(int B, int N, int Hq, int d, int splits) {
   return w;
 }
 
-template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT>
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT, bool NARROW = false>
 hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t stream) {
-  using WG = FwdWG<D, CAUSAL, SPARSE, SPLIT>;
+  using WG = FwdWG<D, CAUSAL, SPARSE, SPLIT, NARROW>;
   const int nblk = (a.N + WG::BM - 1) / WG::BM;
   const long long total = (long long)nblk * a.Hq * a.B;
   if (total > 0x7fffffffLL) return hipErrorInvalidConfiguration;
@@ -707,7 +717,7 @@ hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t stream) {
   if (SPLIT && (a.splits < 1 || a.splits > 65535 || a.split_len < 1 || a.split_len % SPARSE_BLOCK != 0 ||
                 a.opart == nullptr || a.lsepart == nullptr))
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, SPARSE, SPLIT>), dim3((unsigned)total, SPLIT ? a.splits : 1),
+  hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, SPARSE, SPLIT, NARROW>), dim3((unsigned)total, SPLIT ? a.splits : 1),
                      dim3(WG::THREADS), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (!SPLIT || e != hipSuccess) return e;
@@ -722,6 +732,9 @@ template <typename Tag, int D, bool CAUSAL>
 hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   if (a.sp.bmask) return launch_fwd_s<Tag, D, CAUSAL, true, false>(a, stream);
   if (a.splits > 1 || a.opart) return launch_fwd_s<Tag, D, CAUSAL, false, true>(a, stream);
+  if constexpr (!CAUSAL && D <= 128) {
+    if (a.Nk <= NarrowKeys<D>::MAX) return launch_fwd_s<Tag, D, false, false, false, true>(a, stream);
+  }
   return launch_fwd_s<Tag, D, CAUSAL, false, false>(a, stream);
 }
 

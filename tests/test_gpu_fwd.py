@@ -61,6 +61,18 @@ def test_small_shapes(gpu_device, b, n, hq, hkv, d, dtype, causal):
     _check_full(x, o, lse, causal, scale, f"b{b} n{n} hq{hq} hkv{hkv} d{d} {dtype} causal={causal}", dtype)
 
 
+# Non-causal forwards run four-wavefront workgroups up to 2048 keys at d = 128
+# and 8192 at d = 64, eight beyond; these sit just past those key counts, so
+# the eight-wavefront path (ragged last tile included) is checked on every
+# element too, not only on the sampled rows of the full-size workloads.
+@pytest.mark.parametrize("b,n,hq,hkv,d,dtype", [(1, 2100, 2, 1, 128, "bf16"), (1, 8250, 1, 1, 64, "fp16")])
+def test_eight_wavefront_path(gpu_device, b, n, hq, hkv, d, dtype):
+    x = gen.make_inputs(b, n, hq, hkv, d, dtype, cfg_id=7, seed=n, with_do=False)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = run_fwd(x, dtype, False, scale, gpu_device)
+    _check_full(x, o, lse, False, scale, f"b{b} n{n} hq{hq} hkv{hkv} d{d} {dtype} non-causal", dtype)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])
 @pytest.mark.parametrize("causal", [False, True])
 def test_unusual_scales(gpu_device, scale, causal):
