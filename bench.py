@@ -250,7 +250,8 @@ def run(args):
 
 
 def sweep():
-    """Per-configuration forward / backward throughput (HIP events, median of 10)."""
+    """Per-configuration forward / backward throughput (HIP events, median of 10
+    after at least 100 ms of warm-up launches of the same configuration)."""
     import numpy as np
     import torch
 
@@ -278,8 +279,16 @@ def sweep():
         res = {}
         for name, fn in (("fwd", lambda: ea.attn_fwd(q, k, v, o, lse, s.causal, sc, stream)),
                          ("bwd", lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, s.causal, sc, stream))):
-            for _ in range(3):
+            # warm-up of at least 100 ms of this workload's own launches, so
+            # that the clock state left by the previous workload has passed
+            t0 = time.perf_counter()
+            n_warm = 0
+            while n_warm < 3 or time.perf_counter() - t0 < 0.1:
                 fn()
+                n_warm += 1
+                if n_warm % 8 == 0:
+                    stream.synchronize()
+            stream.synchronize()
             ts = []
             for _ in range(10):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -799,7 +808,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed steps before the timed ones (40 steps, about 0.14 s, let the clock settle)")
     ap.add_argument("--sweep", action="store_true", help="also time every full-size configuration")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline budget in seconds (0 disables it)")
