@@ -433,6 +433,10 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         if (V_LDS) va[i] = fr.row(vblk, wave, kk);
       };
       rd(0, 0);
+      // Issue priority: while a wavefront runs a block of products it issues
+      // ahead of the other wavefront on its SIMD, which meanwhile runs its
+      // exponentials; the matrix pipe then sees fewer gaps (3-4% on this pass).
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         if (kk + 1 < NKK) rd(kk + 1, (kk + 1) & 1);
@@ -442,6 +446,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         if (kk + 1 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, V_LDS ? 3 : 2, 0);  // DS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                // MFMA
       }
+      __builtin_amdgcn_s_setprio(0);
     }
     // P = 2^(S c - LSE2), dS = P (dP - D)
     const int klim = mykey - a.coff - q0 - 4 * half;
@@ -477,6 +482,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
       };
 #pragma unroll
       for (int f = 0; f < PFT; ++f) ta[f] = rd(f);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         if (f + PFT < NF) ta[(f + PFT) % (PFT + 1)] = rd(f + PFT);
@@ -488,6 +494,7 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
         if (f + PFT < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
       }
+      __builtin_amdgcn_s_setprio(0);
     }
   };
 
