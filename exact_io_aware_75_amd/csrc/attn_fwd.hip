@@ -508,7 +508,11 @@ attn_fwd_kernel(FwdArgs a) {
       }
     };
     if constexpr (HAS_NEXT) {
+      // the next tile's products (this tile's softmax interleaved) issue at
+      // raised priority, ahead of the other wavefront on the SIMD (about 1%)
+      __builtin_amdgcn_s_setprio(1);
       scores(knext, s_next, hook);
+      __builtin_amdgcn_s_setprio(0);
     } else {
       static_for<0, NKK>(hook);
     }
