@@ -157,12 +157,16 @@ def attention_head_fwd(q, k, v, causal: bool, scale: float, rows=None, chunk: in
 
 
 def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk: int = 512,
-                       head_mask=None, block: int = 128, causal_offset=None):
+                       head_mask=None, block: int = 128, causal_offset=None, cols=None):
     """Gradients of L = sum(O * dO) for one query head.
 
     Returns (dq_rows, dk, dv): dq for the query ``rows`` (default: all) and this
     head's whole contribution to dK and dV of its K/V head.  dK/dV need every
-    query row, so they are only returned when ``rows`` is None.
+    query row, so they are only returned when ``rows`` is None.  ``cols``
+    (optional key indices) restricts dK/dV to those keys: the same sums over
+    every query row, kept only for the listed columns ([len(cols), d] each),
+    so that long sequences can be checked key by key; dq is then not formed
+    (returned as None).
     """
     q = np.asarray(q, dtype=_F)
     k = np.asarray(k, dtype=_F)
@@ -170,10 +174,12 @@ def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk
     do = np.asarray(do, dtype=_F)
     full = rows is None
     rows = np.arange(q.shape[0]) if full else np.asarray(rows, dtype=np.int64)
+    cols = None if cols is None else np.asarray(cols, dtype=np.int64)
     off = _offset(causal_offset, q.shape[0], k.shape[0])
-    dq = np.empty((len(rows), q.shape[1]), dtype=_F)
-    dk = np.zeros_like(k) if full else None
-    dv = np.zeros_like(v) if full else None
+    dq = np.empty((len(rows), q.shape[1]), dtype=_F) if cols is None else None
+    kc = k if cols is None else k[cols]
+    dk = np.zeros_like(kc) if full else None
+    dv = np.zeros((kc.shape[0], v.shape[1]), dtype=_F) if full else None
     for c0 in range(0, len(rows), chunk):
         r = rows[c0:c0 + chunk]
         s = scale * (q[r] @ k.T)
@@ -181,10 +187,12 @@ def attention_head_bwd(q, k, v, do, causal: bool, scale: float, rows=None, chunk
         dp = do[r] @ v.T
         dsum = (p * dp).sum(axis=1)
         ds = p * (dp - dsum[:, None])
-        dq[c0:c0 + chunk] = scale * (ds @ k)
+        if dq is not None:
+            dq[c0:c0 + chunk] = scale * (ds @ k)
         if full:
-            dk += scale * (ds.T @ q[r])
-            dv += p.T @ do[r]
+            pc, dsc = (p, ds) if cols is None else (p[:, cols], ds[:, cols])
+            dk += scale * (dsc.T @ q[r])
+            dv += pc.T @ do[r]
     return dq, dk, dv
 
 

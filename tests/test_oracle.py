@@ -130,6 +130,56 @@ def test_softmax_rows_sum_to_one(causal):
         assert (np.triu(p, 1) == 0).all()
 
 
+
+def test_probs_hand_worked():
+    """The materialised P of the hand-worked 2 x 2 example, at scale 1 and at
+    scale 2 (where a dropped or doubled scale changes every row-0 entry)."""
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_n2_d1.json")))
+    q, k = np.array(g["q"]).reshape(2, 1), np.array(g["k"]).reshape(2, 1)
+    for sc, key in ((1.0, "scale_1"), (2.0, "scale_2")):
+        for causal in (False, True):
+            p = oracle.attention_head_probs(q, k, causal, sc)
+            np.testing.assert_allclose(p, g["probs"][key]["causal" if causal else "noncausal"], atol=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probs_agree_with_output_and_lse(causal):
+    """P ties to the pinned forward: P V equals O, and on every allowed entry
+    ln P = scale * <q_i, k_j> - LSE_i (exactly the softmax in log form)."""
+    x = make_inputs(1, 37, 1, 1, 8, "bf16", cfg_id=97)
+    q, k, v = (x[t][0, :, 0].astype(np.float64) for t in ("q", "k", "v"))
+    scale = 0.45
+    p = oracle.attention_head_probs(q, k, causal, scale)
+    o, lse = oracle.attention_head_fwd(q, k, v, causal, scale)
+    np.testing.assert_allclose(p @ v, o, atol=1e-13)
+    allowed = np.tril(np.ones((37, 37), dtype=bool)) if causal else np.ones((37, 37), dtype=bool)
+    s = scale * np.einsum("id,jd->ij", q, k)
+    np.testing.assert_allclose(np.log(p[allowed]), (s - lse[:, None])[allowed], atol=1e-12)
+    assert (p[~allowed] == 0).all()
+
+
+def test_planted_probs_mistake_is_caught(monkeypatch):
+    """A probability matrix that forgets the scale fails the scale-2 golden."""
+    real = oa._row_softmax
+    monkeypatch.setattr(oa, "_row_softmax", lambda s, allowed: real(s / 2.0, allowed))
+    g = json.load(open(os.path.join(GOLDEN, "hand_worked_n2_d1.json")))
+    q, k = np.array(g["q"]).reshape(2, 1), np.array(g["k"]).reshape(2, 1)
+    p = oracle.attention_head_probs(q, k, False, 2.0)
+    assert np.abs(p - np.array(g["probs"]["scale_2"]["noncausal"])).max() > 1e-3
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_key_subset_gradients_match_full(causal):
+    """dK/dV restricted to a set of keys are those keys' rows of the full dK/dV."""
+    x = make_inputs(1, 90, 1, 1, 16, "bf16", cfg_id=96)
+    q, k, v, do = (x[t][0, :, 0] for t in ("q", "k", "v", "do"))
+    cols = np.array([0, 1, 31, 32, 64, 89])
+    _, dk, dv = oracle.attention_head_bwd(q, k, v, do, causal, 0.3, chunk=17)
+    dq_c, dk_c, dv_c = oracle.attention_head_bwd(q, k, v, do, causal, 0.3, chunk=17, cols=cols)
+    assert dq_c is None
+    np.testing.assert_allclose(dk_c, dk[cols], atol=1e-14)
+    np.testing.assert_allclose(dv_c, dv[cols], atol=1e-14)
+
 def _n_allowed(n, causal):
     return np.arange(1, n + 1) if causal else np.full(n, n)
 
