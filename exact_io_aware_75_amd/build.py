@@ -23,11 +23,15 @@ SOURCES = ("attn_api.hip", "attn_fwd.hip", "attn_bwd.hip", "attn_std.hip")
 # The MFMA throughput probe the benchmark measures its ceiling with: a
 # separate library, not part of the attention ABI.
 PROBE_SOURCES = ("mfma_probe.hip",)
-# Per-file extra flags.  The forward kernel never produces NaN from finite
-# inputs (masked scores are -inf, never NaN), so NaN-preserving max semantics
-# are dropped there: v_max3 then needs no canonicalising v_max per MFMA result.
-# Host-side argument validation (attn_api.hip, which tests for NaN scales)
-# keeps full IEEE semantics.
+# Per-file extra flags.  The forward kernel forms no NaN from finite inputs
+# in any value it uses: masked scores are -inf, and where -inf could meet -inf
+# or 0 (the scaled row max of a row with no key in a tile when scale = 0; the
+# rescale factor, probability shift and final division of a row that has no
+# key) it selects -inf, 1, 0 or 0 instead.  The one NaN left, a masked score
+# times scale 0 inside exp2, is discarded by a select on the score.  So
+# NaN-preserving max semantics are dropped there: v_max3 then needs no
+# canonicalising v_max per MFMA result.  Host-side argument validation
+# (attn_api.hip, which tests for NaN scales) keeps full IEEE semantics.
 FILE_FLAGS = {"attn_fwd.hip": ["-fno-honor-nans"]}
 LIB = os.path.join(HERE, "libattn.so")
 PROBE_LIB = os.path.join(HERE, "libattn_probe.so")

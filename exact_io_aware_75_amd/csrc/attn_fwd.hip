@@ -400,11 +400,15 @@ attn_fwd_kernel(FwdArgs a) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
                                                      __builtin_bit_cast(uint32_t, mx), false, false);
     mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
-    const float mxs = mx * c;
+    // Causal, a row can have no allowed key in a tile (mx = -inf; with scale
+    // 0, -inf * 0 would be NaN, so the select keeps -inf) and no key at all so
+    // far (m_new = -inf; its probabilities are then shifted by 0, not +inf).
+    // Without a mask every tile gives every row a key.
+    const float mxs = (CAUSAL && mx == -INFINITY) ? -INFINITY : mx * c;
     // deferred rescale: move the reference max only when it grows by > 2^8
     st.need = __builtin_amdgcn_ballot_w64(mxs > m_ref + RESCALE_THRESHOLD) != 0;
     st.m_new = st.need ? fmaxf(m_ref, mxs) : m_ref;
-    st.nm = -st.m_new;
+    st.nm = (CAUSAL && st.m_new == -INFINITY) ? 0.f : -st.m_new;
   };
   // probability pairs [p0, p1) of the tile, pair index = 4 * key-k-step + t
   auto probs = [&](const f32x16_t* s, SoftState& st, int p0, int p1, auto mask_tag) __attribute__((always_inline)) {
@@ -445,7 +449,9 @@ attn_fwd_kernel(FwdArgs a) {
   // move the reference max (rare) -- after the probabilities, before P V
   auto rescale = [&](SoftState& st) __attribute__((always_inline)) {
     if (st.need) {
-      const float alpha = fast_exp2(m_ref - st.m_new);
+      // a lane whose row has seen no key yet keeps m_new = -inf: its factor
+      // is 1 (the accumulators are still zero), not exp2(-inf + inf) = NaN
+      const float alpha = (CAUSAL && st.m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - st.m_new);
 #pragma unroll
       for (int t = 0; t < 4; ++t) lsum[t] *= alpha;
 #pragma unroll
@@ -618,12 +624,12 @@ attn_fwd_kernel(FwdArgs a) {
                                                      __builtin_bit_cast(uint32_t, ls), false, false);
     ltot = __builtin_bit_cast(float, (uint32_t)sw[0]) + __builtin_bit_cast(float, (uint32_t)sw[1]);
   }
-  // A row with no allowed key (causal, qrow + coff < 0; its accumulators
-  // are not meaningful) gets O = 0 and LSE = -inf; the test is on integers.
+  // A row with no allowed key (causal, qrow + coff < 0) gets O = 0 and
+  // LSE = -inf; the test is on integers (its sum is 0).
   const bool empty = CAUSAL && qrow + coff < 0;
   if (SPLIT) {  // fp32 partials, each normalised by its own sum
     if (qvalid) {
-      const float inv = 1.0f / ltot;
+      const float inv = empty ? 0.f : 1.0f / ltot;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -638,7 +644,7 @@ attn_fwd_kernel(FwdArgs a) {
     return;
   }
   if (qvalid) {
-    const float inv = 1.0f / ltot;
+    const float inv = empty ? 0.f : 1.0f / ltot;
     uint16_t* orow = (uint16_t*)a.o + ((size_t)b * a.N * a.Hq + h) * D + (size_t)qrow * q_row;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)

@@ -73,6 +73,35 @@ def test_small_shapes(gpu_device, b, nq, nk, hq, hkv, d, dtype, causal, offset):
     _check(x, out, causal, offset, scale, tag, dtype)
 
 
+
+# scale = 0 with a causal offset that is not a multiple of 32: rows with no
+# key sit in the same wavefronts as rows with keys, and diagonal tiles are
+# fully masked for some rows, where the scaled row max would be -inf * 0.
+# With scale 0 every visible key has probability 1 / (number visible).
+@pytest.mark.parametrize("b,nq,nk,hq,hkv,d,dtype,offset", [
+    (1, 300, 400, 2, 1, 128, "bf16", -45),
+    (1, 257, 700, 2, 2, 64, "fp16", -77),
+    (1, 200, 500, 2, 2, 256, "bf16", -13),
+])
+def test_scale_zero_with_empty_rows(gpu_device, b, nq, nk, hq, hkv, d, dtype, offset):
+    x = make_rect_inputs(b, nq, nk, hq, hkv, d, dtype, cfg_id=43, seed=nq)
+    tag = f"rect scale=0 b{b} nq{nq} nk{nk} hq{hq} hkv{hkv} d{d} {dtype} offset={offset}"
+    log(tag)
+    out = run_fwd_bwd(x, dtype, True, 0.0, gpu_device, causal_offset=offset)
+    _check(x, out, True, offset, 0.0, tag, dtype)
+    o, lse = out[0], out[1]
+    v = x["v"].astype(np.float64)
+    for i in (0, -offset - 1, -offset, -offset + 1, nq - 1):  # closed form: prefix means of V
+        if 0 <= i < nq:
+            nvis = min(max(i + offset + 1, 0), nk)
+            if nvis == 0:
+                assert (o[:, i] == 0).all() and (lse[:, :, i] == -np.inf).all()
+            else:
+                rep = hq // hkv
+                mean = np.repeat(v[:, :nvis].mean(axis=1), rep, axis=1)
+                assert np.abs(o[:, i] - mean).max() <= TOL_O
+                assert np.abs(lse[:, :, i] - np.log(nvis)).max() <= TOL_LSE
+
 def test_square_offset_zero_is_attn_fwd_bitwise(gpu_device):
     import torch
     import exact_io_aware_75_amd as ea
