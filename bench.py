@@ -15,8 +15,14 @@ Prints one JSON line.  Besides the throughput it carries
                 own stream, against the dense bf16 MFMA peak; `traffic` is the HBM
                 bytes per launch measured with rocprofv3 counters for the current
                 kernel source (null when the source changed since);
+  targets       forward and backward TFLOP/s at the points the forward target
+                is stated for (d = 128, N = 4096 and 16384) and at d = 64
+                (N = 4096 and 16384), causal and not, each after its own
+                warm-up (HIP events, median of 10);
   cpu_baseline  the CPU fp64 oracle timed on a bounded sample of the same
-                workload on this host;
+                workload on this host: whole (batch, head) slices, one per
+                worker process over the host's cores, with the core count,
+                CPU model and BLAS threads recorded;
   blocksparse   block-sparse attention (attn_fwd_blocksparse /
                 attn_bwd_blocksparse) on its own workload -- hidden 2048,
                 d = 128, B = 1, N = 16384, one block mask with every diagonal
@@ -42,7 +48,8 @@ Prints one JSON line.  Besides the throughput it carries
                 speed-ups over the hidden-2048, d = 128 sequence-length sweep
                 (B * N = 16384).
 --sweep also prints per-workload forward/backward TFLOP/s for every full-size
-configuration to stderr.
+configuration to stderr; --oracle-sweep times the CPU oracle (fwd, fwd+bwd)
+on every full-size configuration and exits.
 """
 
 from __future__ import annotations
@@ -88,45 +95,151 @@ def load_traffic():
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline(seconds: float):
-    """Time the fp64 oracle on whole (batch, head) slices of the workload."""
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl is optional
+        return 0
+
+
+def _pool_workers() -> int:
+    """Worker processes for the oracle: the host cores this process may use,
+    capped by OMP_NUM_THREADS when it is set (the CPU share of the machine)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    cap = os.environ.get("OMP_NUM_THREADS", "")
+    if cap.isdigit() and int(cap) > 0:
+        n = min(n, int(cap))
+    return max(1, n)
+
+
+def _oracle_slice(task):
+    """One whole (batch, head) slice of the oracle, fwd then bwd (a worker
+    process with one BLAS thread).  Returns (fwd seconds, fwd+bwd seconds).
+    ``rows`` < N times only the first ``rows`` queries against all keys
+    (non-causal: the oracle forms the full score rows either way)."""
     import numpy as np
 
     import oracle
     from exact_io_aware_75_amd import inputs as gen
 
-    try:
-        from threadpoolctl import threadpool_info
+    n, d, causal, seed, rows = task
+    x = gen.make_inputs(1, n, 1, 1, d, "bf16", cfg_id=3, seed=seed)
+    q, k, v, do = (x[t][0, :, 0] for t in ("q", "k", "v", "do"))
+    if rows < n:
+        q, do, causal = q[:rows], do[:rows], False
+    scale = 1.0 / np.sqrt(d)
+    t0 = time.perf_counter()
+    oracle.attention_head_fwd(q, k, v, causal, scale)
+    t1 = time.perf_counter()
+    oracle.attention_head_bwd(q, k, v, do, causal, scale)
+    t2 = time.perf_counter()
+    return t1 - t0, t2 - t0
 
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover - threadpoolctl is optional
-        cores = os.cpu_count() or 1
+
+def _oracle_pool(workers):
+    import multiprocessing as mp
+
+    # one BLAS thread per worker process; set before the children start
+    saved = {k_: os.environ.get(k_) for k_ in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k_ in saved:
+        os.environ[k_] = "1"
+    try:
+        pool = mp.get_context("spawn").Pool(workers)
+    finally:
+        for k_, v_ in saved.items():
+            if v_ is None:
+                os.environ.pop(k_, None)
+            else:
+                os.environ[k_] = v_
+    return pool
+
+
+def cpu_baseline(seconds: float):
+    """Time the fp64 oracle on whole (batch, head) slices of the workload, one
+    slice per worker process over the host's cores, for about ``seconds`` of
+    wall clock."""
     w = WORKLOAD
     n, d = w["n"], w["d"]
-    rng = np.random.default_rng(0)
-    flops = 0.0
-    slices = 0
-    elapsed = 0.0  # oracle time only; input generation is not counted
-    while elapsed < seconds:
-        causal = slices % 2 == 1
-        seed = int(rng.integers(1 << 30))
-        x = gen.make_inputs(1, n, 1, 1, d, "bf16", cfg_id=3, seed=seed)
-        q, k, v, do = (x[t][0, :, 0] for t in ("q", "k", "v", "do"))
-        scale = 1.0 / np.sqrt(d)
-        ts = time.perf_counter()
-        oracle.attention_head_fwd(q, k, v, causal, scale)
-        oracle.attention_head_bwd(q, k, v, do, causal, scale)
-        elapsed += time.perf_counter() - ts
-        flops += 3.5 * fwd_flops(1, n, 1, d, causal)
-        slices += 1
+    workers = _pool_workers()
+    pool = _oracle_pool(workers)
+    try:
+        pool.map(_oracle_slice, [(256, d, False, 0, 256)] * workers)  # start-up and imports, untimed
+        flops = 0.0
+        slices = 0
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            tasks = [(n, d, (slices + i) % 2 == 1, 1000 + slices + i, n) for i in range(workers)]
+            pool.map(_oracle_slice, tasks)
+            flops += sum(3.5 * fwd_flops(1, n, 1, d, t[2]) for t in tasks)
+            slices += len(tasks)
+        elapsed = time.perf_counter() - t0
+    finally:
+        pool.close()
+        pool.join()
     return {
         "value": flops / elapsed / 1e12,
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": workers,
         "kind": "oracle",
         "sample": f"{slices} (batch, head) slices of N={n}, d={d} (alternately non-causal and causal), "
-                  f"fwd+bwd in fp64, {elapsed:.1f} s; FLOPs counted as for the GPU",
+                  f"fwd+bwd in fp64, {workers} worker processes x 1 BLAS thread, {elapsed:.1f} s wall; "
+                  f"FLOPs counted as for the GPU (causal halved, although the oracle forms every score)",
+        "host": {"os_cpu_count": os.cpu_count(), "cpu_model": _cpu_model(),
+                 "blas_threads_in_parent": _blas_threads(), "workers": workers},
     }
+
+
+def oracle_sweep(max_rows: int = 4096):
+    """Wall clock of the fp64 oracle per full-size workload, fwd and fwd+bwd,
+    on the host's cores (one (batch, head) slice per worker).  Slices of more
+    than ``max_rows`` queries are timed on their first ``max_rows`` rows
+    against all keys and scaled by N / max_rows (the oracle's cost is linear
+    in the rows); those points are marked extrapolated."""
+    from exact_io_aware_75_amd import configs
+
+    workers = _pool_workers()
+    pool = _oracle_pool(workers)
+    out = []
+    try:
+        pool.map(_oracle_slice, [(256, 64, False, 0, 256)] * workers)
+        for s in configs.all_shapes()[1:]:
+            slices = s.b * s.hq
+            rows = min(s.n, max_rows)
+            tasks = [(s.n, s.d, s.causal, 7 + i, rows) for i in range(min(workers, slices))]
+            t0 = time.perf_counter()
+            res = pool.map(_oracle_slice, tasks)
+            wall = time.perf_counter() - t0
+            rounds = -(-slices // workers)
+            scale_rows = s.n / rows
+            fwd_share = sum(r[0] for r in res) / max(sum(r[1] for r in res), 1e-30)
+            total = wall * rounds * scale_rows
+            rec = {"workload": s.name, "B": s.b, "N": s.n, "Hq": s.hq, "Hkv": s.hkv, "d": s.d,
+                   "causal": s.causal, "fwd_s": round(total * fwd_share, 2), "fwd_bwd_s": round(total, 2),
+                   "workers": workers, "extrapolated": rows < s.n or rounds > 1,
+                   "how": f"{len(tasks)} slices of {rows}/{s.n} rows in parallel took {wall:.2f} s; "
+                          f"x {rounds} rounds of {workers} slices" + (f" x {scale_rows:g} rows" if rows < s.n else "")}
+            print("oracle " + json.dumps(rec), file=sys.stderr, flush=True)
+            out.append(rec)
+    finally:
+        pool.close()
+        pool.join()
+    return out
 
 
 def run(args):
@@ -231,6 +344,8 @@ def run(args):
         "kernel_ms": {k_: round(v_, 4) for k_, v_ in mean.items()},
         "roofline": roofline,
     }
+    if args.targets:
+        line["targets"] = targets_measure()
     if args.sparse:
         line["blocksparse"] = blocksparse_measure()
         line["shard"] = shard_measure()
@@ -249,63 +364,90 @@ def run(args):
     print(json.dumps(line), flush=True)
 
 
-def sweep():
-    """Per-configuration forward / backward throughput (HIP events, median of 10
-    after at least 100 ms of warm-up launches of the same configuration)."""
+def measure_shape(s, reps=10, seed=0):
+    """Forward and backward of one workload (torch.randn inputs rounded to
+    bf16): HIP events on the launch stream, median of ``reps`` launches after
+    at least 100 ms of warm-up launches of the same workload, so that the
+    clock state left by the previous workload has passed.  Returns
+    {"fwd": (ms, TFLOP/s), "bwd": (ms, TFLOP/s)}."""
     import numpy as np
     import torch
 
     import exact_io_aware_75_amd as ea
-    from exact_io_aware_75_amd import configs
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
-    shapes = []
-    for d in (64, 128):
-        for n in configs.SWEEP_N:
-            for c in (False, True):
-                shapes.append(configs.hidden2048(d, n, c))
-    shapes += [configs.long_seq(32768), configs.long_seq(65536), configs.gqa(8), configs.gqa(1),
-               configs.wide_head()]
     gen = torch.Generator(device=dev)
-    gen.manual_seed(0)
-    for s in shapes:
-        mk = lambda hh: torch.randn(s.b, s.n, hh, s.d, device=dev, generator=gen).to(torch.bfloat16)  # noqa: E731
-        q, k, v, do = mk(s.hq), mk(s.hkv), mk(s.hkv), mk(s.hq)
-        o, lse = torch.empty_like(q), torch.empty((s.b, s.hq, s.n), dtype=torch.float32, device=dev)
-        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-        ws = torch.empty(ea.attn_bwd_workspace_bytes(s.b, s.n, s.hq, s.hkv, s.d), dtype=torch.uint8, device=dev)
-        sc = 1.0 / float(np.sqrt(s.d))
-        res = {}
-        for name, fn in (("fwd", lambda: ea.attn_fwd(q, k, v, o, lse, s.causal, sc, stream)),
-                         ("bwd", lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, s.causal, sc, stream))):
-            # warm-up of at least 100 ms of this workload's own launches, so
-            # that the clock state left by the previous workload has passed
-            t0 = time.perf_counter()
-            n_warm = 0
-            while n_warm < 3 or time.perf_counter() - t0 < 0.1:
-                fn()
-                n_warm += 1
-                if n_warm % 8 == 0:
-                    stream.synchronize()
-            stream.synchronize()
-            ts = []
-            for _ in range(10):
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                fn()
-                e1.record(stream)
-                e1.synchronize()
-                ts.append(e0.elapsed_time(e1))
-            t = float(np.median(ts))
-            fl = s.fwd_flops() * (2.5 if name == "bwd" else 1.0)
-            res[name] = (t, fl / (t / 1e3) / 1e12)
+    gen.manual_seed(seed)
+    mk = lambda hh: torch.randn(s.b, s.n, hh, s.d, device=dev, generator=gen).to(torch.bfloat16)  # noqa: E731
+    q, k, v, do = mk(s.hq), mk(s.hkv), mk(s.hkv), mk(s.hq)
+    o, lse = torch.empty_like(q), torch.empty((s.b, s.hq, s.n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(s.b, s.n, s.hq, s.hkv, s.d), dtype=torch.uint8, device=dev)
+    sc = 1.0 / float(np.sqrt(s.d))
+    res = {}
+    for name, fn in (("fwd", lambda: ea.attn_fwd(q, k, v, o, lse, s.causal, sc, stream)),
+                     ("bwd", lambda: ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, s.causal, sc, stream))):
+        t0 = time.perf_counter()
+        n_warm = 0
+        while n_warm < 3 or time.perf_counter() - t0 < 0.1:
+            fn()
+            n_warm += 1
+            if n_warm % 8 == 0:
+                stream.synchronize()
+        stream.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        t = float(np.median(ts))
+        fl = s.fwd_flops() * (2.5 if name == "bwd" else 1.0)
+        res[name] = (t, fl / (t / 1e3) / 1e12)
+    del q, k, v, do, o, lse, dq, dk, dv, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+# The points the forward target is stated for (d = 128, N >= 4k) and the
+# d = 64 half of the metric, on the hidden-2048 layer (B * N = 16384).
+TARGET_POINTS = ((128, 4096), (128, 16384), (64, 4096), (64, 16384))
+
+
+def targets_measure():
+    from exact_io_aware_75_amd import configs
+
+    out = {}
+    for d, n in TARGET_POINTS:
+        for c in (False, True):
+            s = configs.hidden2048(d, n, c)
+            r = measure_shape(s)
+            out[f"d{d}_n{n}_{'causal' if c else 'noncausal'}"] = {
+                "B": s.b, "N": s.n, "H": s.hq, "d": s.d, "causal": c,
+                "fwd_ms": round(r["fwd"][0], 4), "fwd_tflops": round(r["fwd"][1], 1),
+                "fwd_frac_of_peak": round(r["fwd"][1] / PEAK_BF16_TFLOPS, 4),
+                "bwd_ms": round(r["bwd"][0], 4), "bwd_tflops": round(r["bwd"][1], 1),
+                "bwd_frac_of_peak": round(r["bwd"][1] / PEAK_BF16_TFLOPS, 4)}
+    return {"what": "hidden-2048 layer (B * N = 16384, H = 2048 / d), bf16, scale 1/sqrt(d); HIP events on the "
+                    "launch stream, median of 10 after >= 100 ms of warm-up launches of the same workload; "
+                    "backward = 2.5 x forward FLOPs, causal halved",
+            "points": out}
+
+
+def sweep():
+    """Per-configuration forward / backward throughput for every full-size
+    workload (``measure_shape``), printed to stderr."""
+    from exact_io_aware_75_amd import configs
+
+    for s in configs.all_shapes()[1:]:
+        res = measure_shape(s)
         print(f"sweep {s.name:16s} B={s.b:2d} N={s.n:6d} Hq={s.hq:2d} Hkv={s.hkv:2d} d={s.d:3d} causal={int(s.causal)}  "
               f"fwd {res['fwd'][0]:8.3f} ms {res['fwd'][1]:7.1f} TFLOP/s ({100 * res['fwd'][1] / PEAK_BF16_TFLOPS:4.1f}%)  "
               f"bwd {res['bwd'][0]:8.3f} ms {res['bwd'][1]:7.1f} TFLOP/s ({100 * res['bwd'][1] / PEAK_BF16_TFLOPS:4.1f}%)",
               file=sys.stderr, flush=True)
-        del q, k, v, do, o, lse, dq, dk, dv, ws
-        torch.cuda.empty_cache()
 
 
 def _median_ms(fn, stream, reps=10):
@@ -814,6 +956,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline budget in seconds (0 disables it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--oracle-sweep", action="store_true",
+                    help="time the CPU fp64 oracle on every full-size workload (fwd, fwd+bwd) and exit")
+    ap.add_argument("--no-targets", dest="targets", action="store_false",
+                    help="skip the per-workload target points in the JSON line")
     ap.add_argument("--no-sparse", dest="sparse", action="store_false",
                     help="skip the block-sparse and shard measurements")
     ap.add_argument("--no-standard", dest="standard", action="store_false",
@@ -844,6 +990,9 @@ def main():
               "(the kernels shard trivially over batch and heads; this benchmark measures one GPU).",
               file=sys.stderr)
         sys.exit(2)
+    if args.oracle_sweep:
+        print(json.dumps({"oracle_sweep": oracle_sweep()}), flush=True)
+        return
     if args.no_cpu_baseline:
         args.cpu_seconds = 0.0
     if args.copy_calibration:
