@@ -72,6 +72,20 @@ bool debug_sync() {
   return on;
 }
 
+// ATTN_LAUNCH_TEST in the environment, read on every call (a testing aid
+// for the race checks): "reverse" runs each kernel's workgroups in reversed
+// work-item order, "one_wg_per_cu" pads their LDS so that each CU holds one
+// workgroup at a time.  Results must not change.
+attn::LaunchTest launch_test() {
+  attn::LaunchTest lt = {0, 0};
+  const char* v = std::getenv("ATTN_LAUNCH_TEST");
+  if (v != nullptr) {
+    lt.reverse = std::strcmp(v, "reverse") == 0;
+    lt.one_wg_per_cu = std::strcmp(v, "one_wg_per_cu") == 0;
+  }
+  return lt;
+}
+
 // Result of a call's launches: a launch error, or under ATTN_DEBUG an
 // execution error found by synchronising the stream.
 int finish(hipError_t e, void* stream) {
@@ -172,6 +186,7 @@ int fwd_common(const void* q, const void* k, const void* v, void* o, float* lse,
   a.sp = sp;
   a.Nk = Nk;
   a.coff = clamp_offset(causal_offset, N, Nk);
+  a.lt = launch_test();
   a.splits = 1;
   a.split_len = 0;
   a.opart = nullptr;
@@ -292,6 +307,7 @@ int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, int 
   a.sp = sp;
   a.Nk = Nk;
   a.coff = clamp_offset(causal_offset, N, Nk);
+  a.lt = launch_test();
   a.hsplit = ws.hsplit;
   a.dkv_part = ws.hsplit > 1 ? reinterpret_cast<float*>(static_cast<char*>(workspace) + ws.part_off) : nullptr;
   return finish(attn::launch_bwd(a, dtype == ATTN_DTYPE_BF16, d, causal != 0, stages,

@@ -282,16 +282,17 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   // (d = 256 never splits: its registers are already full)
   const int hs = D <= 128 ? a.hsplit : 1;
   const int nkb = (a.Nk + KV_BN - 1) / KV_BN;
+  const int bid = grid_x(a.lt.reverse);
   int bgs, kb;
   if constexpr (CAUSAL && !SPARSE) {
     // Causal key blocks differ in work (the first sees every query):
     // weight-major order with consecutive work items on consecutive XCDs,
     // as in the causal forward pass.
     const int G = a.Hkv * a.B * hs;
-    kb = blockIdx.x / G;
-    bgs = blockIdx.x - kb * G;
+    kb = bid / G;
+    bgs = bid - kb * G;
   } else {
-    const int Lw = xcd_remap(blockIdx.x, nkb * a.Hkv * a.B * hs);
+    const int Lw = xcd_remap(bid, nkb * a.Hkv * a.B * hs);
     bgs = Lw / nkb;
     kb = Lw - bgs * nkb;
   }
@@ -609,17 +610,18 @@ attn_bwd_dq_kernel(BwdArgs a) {
 
   // ---- which (batch, head, row block) this workgroup owns; heaviest first ----
   const int nblk = (a.N + DQ_BM - 1) / DQ_BM;
+  const int bid = grid_x(a.lt.reverse);
   int bh, rb;
   if constexpr (CAUSAL && !SPARSE) {
     // weight-major, consecutive work items on consecutive XCDs (as in the
     // causal forward pass)
     const int BH = a.Hq * a.B;
-    const int r = blockIdx.x / BH;
-    const int i = blockIdx.x - r * BH;
+    const int r = bid / BH;
+    const int i = bid - r * BH;
     bh = (BH & 7) == 0 ? (i & 7) * (BH >> 3) + (i >> 3) : i;  // contiguous heads per XCD
     rb = nblk - 1 - r;
   } else {
-    const int L = xcd_remap(blockIdx.x, nblk * a.Hq * a.B);
+    const int L = xcd_remap(bid, nblk * a.Hq * a.B);
     bh = L / nblk;
     rb = nblk - 1 - (L - bh * nblk);
   }
@@ -875,8 +877,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
       return hipErrorInvalidValue;
     const long long grid = (long long)((a.Nk + 32 * W - 1) / (32 * W)) * a.Hkv * a.B * a.hsplit;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W), 0,
-                       stream, a);
+    const void* kfn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>);
+    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W),
+                       one_wg_lds_pad(kfn, a.lt.one_wg_per_cu), stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.hsplit > 1) {
@@ -892,8 +895,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     constexpr int W = DqWG<D, CAUSAL, SPARSE>::WAVES;
     const long long grid = (long long)((a.N + 32 * W - 1) / (32 * W)) * a.Hq * a.B;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W), 0,
-                       stream, a);
+    const void* kfn = reinterpret_cast<const void*>(&attn_bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>);
+    hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W),
+                       one_wg_lds_pad(kfn, a.lt.one_wg_per_cu), stream, a);
     return hipGetLastError();
   }
   return hipSuccess;

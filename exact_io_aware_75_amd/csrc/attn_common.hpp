@@ -116,6 +116,22 @@ __device__ __forceinline__ int lds_uniform(const uint16_t* list, int i) {
   return __builtin_amdgcn_readfirstlane((int)list[i]);
 }
 
+// The workgroup's index along x, reversed in the reversed-order test mode.
+__device__ __forceinline__ int grid_x(int reverse) {
+  return reverse ? (int)(gridDim.x - 1 - blockIdx.x) : (int)blockIdx.x;
+}
+
+// Dynamic LDS bytes that keep one workgroup of `kernel` per CU in the
+// one-workgroup-per-CU test mode (its static LDS plus this exceed half of
+// the CU's 160 KiB); 0 otherwise.
+inline size_t one_wg_lds_pad(const void* kernel, int on) {
+  if (!on) return 0;
+  hipFuncAttributes attr;
+  if (hipFuncGetAttributes(&attr, kernel) != hipSuccess) return 0;
+  const size_t half = 80 * 1024;
+  return attr.sharedSizeBytes > half ? 0 : half + 256 - attr.sharedSizeBytes;
+}
+
 // Block index remap so that consecutive logical work items run on the same
 // XCD (the hardware dispatches workgroup i to XCD i % 8).  `total` must be a
 // multiple of 8 for the remap to be a bijection; otherwise identity.

@@ -165,6 +165,7 @@ attn_fwd_kernel(FwdArgs a) {
 
   // ---- which (batch, head, row block) this workgroup owns ----
   const int nblk = (a.N + FWD_BM - 1) / FWD_BM;
+  const int bid = grid_x(a.lt.reverse);
   int bh, rb;
   if constexpr (CAUSAL && !SPARSE) {
     // Causal row blocks differ in work.  Weight-major order: the heaviest
@@ -177,12 +178,12 @@ attn_fwd_kernel(FwdArgs a) {
     // [x B Hq / 8, (x + 1) B Hq / 8), so the query heads of a GQA group and
     // the heads of one batch share K/V in one L2.
     const int BH = a.Hq * a.B;
-    const int r = blockIdx.x / BH;
-    const int i = blockIdx.x - r * BH;
+    const int r = bid / BH;
+    const int i = bid - r * BH;
     bh = (BH & 7) == 0 ? (i & 7) * (BH >> 3) + (i >> 3) : i;
     rb = nblk - 1 - r;
   } else {
-    const int L = xcd_remap(blockIdx.x, nblk * a.Hq * a.B);
+    const int L = xcd_remap(bid, nblk * a.Hq * a.B);
     bh = L / nblk;
     rb = nblk - 1 - (L - bh * nblk);
   }
@@ -727,8 +728,9 @@ hipError_t launch_fwd_s(const FwdArgs& a, hipStream_t stream) {
   if (SPLIT && (a.splits < 1 || a.splits > 65535 || a.split_len < 1 || a.split_len % SPARSE_BLOCK != 0 ||
                 a.opart == nullptr || a.lsepart == nullptr))
     return hipErrorInvalidValue;
+  const void* kfn = reinterpret_cast<const void*>(&attn_fwd_kernel<Tag, D, CAUSAL, SPARSE, SPLIT, NARROW>);
   hipLaunchKernelGGL((attn_fwd_kernel<Tag, D, CAUSAL, SPARSE, SPLIT, NARROW>), dim3((unsigned)total, SPLIT ? a.splits : 1),
-                     dim3(WG::THREADS), 0, stream, a);
+                     dim3(WG::THREADS), one_wg_lds_pad(kfn, a.lt.one_wg_per_cu), stream, a);
   hipError_t e = hipGetLastError();
   if (!SPLIT || e != hipSuccess) return e;
   constexpr int ROWS = 256 / (D / 8);

@@ -21,6 +21,13 @@ struct SparseArgs {
   int mask_hstride;      // entries between the masks of consecutive K/V heads (0: one mask)
 };
 
+// Launch-order test modes (the race checks): the kernels' results must not
+// depend on the order or the concurrency in which workgroups run.
+struct LaunchTest {
+  int reverse;        // 1: workgroup x takes the work item of gridDim.x - 1 - x
+  int one_wg_per_cu;  // 1: dynamic LDS padding keeps every CU to one workgroup
+};
+
 struct FwdArgs {
   const void* q;  // [B, N, Hq, d]
   const void* k;  // [B, Nk, Hkv, d]
@@ -40,6 +47,7 @@ struct FwdArgs {
   int neg_scale;     // 1 if scale < 0 (folded into Q's sign)
   float scale_log2;  // |scale| * log2(e)
   SparseArgs sp;
+  LaunchTest lt;
 };
 
 struct BwdArgs {
@@ -66,6 +74,7 @@ struct BwdArgs {
   // (in split order) into dk, dv.  hsplit = 1: dk, dv written directly.
   int hsplit;
   float* dkv_part;
+  LaunchTest lt;
 };
 
 // Workspace layout of the backward pass (offsets in bytes, 256-byte aligned).
