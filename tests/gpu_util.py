@@ -15,6 +15,16 @@ TOL_LSE = 1e-3
 TOL_GRAD = 2e-2
 
 
+def tol_kv(hq, hkv):
+    """Bound on dK / dV of a K/V head.  They sum the contributions of the
+    Hq / Hkv query heads of its group, each computed from its own rounded
+    probabilities (P and dS enter the matrix products in the 16-bit input
+    type); the stated 2e-2 bounds one head's contribution, and independent
+    rounding errors of Hq / Hkv contributions add in quadrature, so the group
+    sum is held to 2e-2 * sqrt(Hq / Hkv) (2e-2 itself without grouping)."""
+    return TOL_GRAD * float(np.sqrt(hq // hkv))
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()
@@ -85,6 +95,27 @@ def max_err(a, ref):
     diff = np.abs(a - ref)
     i = np.unravel_index(np.argmax(diff), diff.shape) if diff.size else ()
     return (float(diff[i]), float(np.abs(ref[i]))) if diff.size else (0.0, 0.0)
+
+
+def record(tag, name, a, ref, tol, dtype=None):
+    """Flat max-abs error of ``a`` against ``ref`` (and |ref| there), appended
+    as one JSON line to the file named by ATTN_PARITY_LOG, if set, with
+    whether it exceeds the flat bound ``tol`` (i.e. whether the test needed
+    the half-ulp output-rounding allowance of ``excess``).  Returns
+    (error, |ref|)."""
+    import json
+    import os
+
+    err, mag = max_err(a, ref)
+    path = os.environ.get("ATTN_PARITY_LOG")
+    if path:
+        rec = {"case": tag, "tensor": name, "max_abs": err, "ref_at_max": mag, "max_ref": float(np.abs(ref).max()) if ref.size else 0.0,
+               "flat_tol": tol, "within_flat": err <= tol, "checked": int(a.size)}
+        if dtype is not None and ref.size:
+            rec["within_checked_bound"] = excess(a, ref, tol, dtype) <= 0
+        with open(path, "a") as f:
+            f.write(json.dumps(rec) + "\n")
+    return err, mag
 
 
 def full_size_shapes():
