@@ -24,7 +24,8 @@ EXPORTS = ("attn_fwd", "attn_bwd", "attn_bwd_preprocess", "attn_bwd_dkdv", "attn
            "attn_bwd_workspace_bytes", "attn_fwd_blocksparse", "attn_bwd_blocksparse",
            "attn_fwd_rect", "attn_bwd_rect", "attn_fwd_splitkv", "attn_fwd_splitkv_workspace_bytes",
            "attn_fwd_standard", "attn_bwd_standard", "attn_standard_workspace_bytes",
-           "attn_strerror", "attn_last_hip_error", "attn_version")
+           "attn_bwd_noalloc", "attn_strerror", "attn_last_hip_error", "attn_version")
+NOALLOC_SCRATCH_BYTES = 64 << 20  # ATTN_NOALLOC_SCRATCH_BYTES
 SPARSE_BLOCK = 128  # ATTN_SPARSE_BLOCK: rows / keys per block of the block mask
 BWD_STAGES = ("attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq")
 
@@ -58,6 +59,8 @@ def load_library():
         fn = getattr(lib, name)
         fn.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, i, i, i, i, i, i, i, f, vp]
         fn.restype = i
+    lib.attn_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
+    lib.attn_bwd_noalloc.restype = i
     lib.attn_fwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
     lib.attn_fwd_blocksparse.restype = i
     lib.attn_bwd_blocksparse.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp, vp, vp, vp, sz,
@@ -276,6 +279,27 @@ def attn_bwd(q, k, v, o, dout, lse, dq, dk, dv, workspace, causal: bool, scale: 
                                       _ptr(block_mask), mh, *tail)
     if st != 0:
         raise AttnError(st, stage)
+
+
+def attn_bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool, scale: float, stream=None) -> None:
+    """Enqueue ``attn_bwd_noalloc``: the backward pass into preallocated
+    ``dq``, ``dk``, ``dv`` with the library's static device scratch instead of
+    a workspace (calls on one device must not overlap)."""
+    import torch
+
+    lib = load_library()
+    b, n, hq, hkv, d = _dims(q, k)
+    for t, shp, nm in ((q, (b, n, hq, d), "q"), (k, (b, n, hkv, d), "k"),
+                       (v, (b, n, hkv, d), "v"), (o, (b, n, hq, d), "o"),
+                       (dout, (b, n, hq, d), "dout"), (dq, (b, n, hq, d), "dq"),
+                       (dk, (b, n, hkv, d), "dk"), (dv, (b, n, hkv, d), "dv")):
+        _check(t, shp, q.dtype, q.device, nm)
+    _check(lse, (b, hq, n), torch.float32, q.device, "lse")
+    st = lib.attn_bwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                              _ptr(dv), b, n, hq, hkv, d, _dtype_code(q), int(bool(causal)), float(scale),
+                              _stream(stream, q.device))
+    if st != 0:
+        raise AttnError(st, "attn_bwd_noalloc")
 
 
 def attn_standard_workspace_bytes(b: int, n: int, hq: int, hkv: int, d: int) -> int:

@@ -5,6 +5,7 @@
 
 #include <atomic>
 #include <cmath>
+#include <mutex>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -262,7 +263,7 @@ int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, int 
                long long causal_offset, const void* q, const void* k, const void* v, const void* o,
                const void* dout, const float* lse, void* dq, void* dk, void* dv, void* workspace,
                size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype, int causal,
-               float scale, void* stream) {
+               float scale, void* stream, bool allow_split = true) {
   if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULLPTR;
   int st = check_shape(B, N, Hq, Hkv, d);
   if (st != ATTN_OK) return st;
@@ -274,7 +275,7 @@ int bwd_common(int stages, const unsigned char* block_mask, int mask_heads, int 
     if (!aligned16(p)) return ATTN_ERR_ALIGN;
   if (!std::isfinite(scale)) return ATTN_ERR_SCALE;
   // the dK/dV head split serves the square dense pass only
-  const bool split_ok = block_mask == nullptr && mask_heads == 0 && Nk == N;
+  const bool split_ok = allow_split && block_mask == nullptr && mask_heads == 0 && Nk == N;
   const attn::BwdWorkspace ws = attn::bwd_workspace_layout(B, N, Hq, Hkv, d, split_ok);
   if (!workspace || workspace_bytes < ws.total) return ATTN_ERR_WORKSPACE;
   if (!aligned16(workspace)) return ATTN_ERR_ALIGN;
@@ -354,6 +355,69 @@ int attn_bwd_blocksparse(const void* q, const void* k, const void* v, const void
 #undef ATTN_BWD_PASS
 
 }  // extern "C"
+
+// ---- backward with no device allocation: a static scratch array ----
+
+namespace {
+
+constexpr size_t kNoAllocScratch = ATTN_NOALLOC_SCRATCH_BYTES;
+// The backward's scratch for callers that cannot allocate: D and, where they
+// fit beside it, the fp32 dK/dV partials of a split GQA group.  Each device
+// the library runs on holds its own copy until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in for
+// the symbol); it uses the device address from scratch_address().
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device (with that device current) and kept.
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_hip_error = (int)e;
+    return ATTN_ERR_DEVICE;
+  }
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr) {
+        g_last_hip_error = (int)e;
+        return ATTN_ERR_HIP;
+      }
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return ATTN_OK;
+}
+
+}  // namespace
+
+extern "C" int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                                const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                                int N, int Hq, int Hkv, int d, int dtype, int causal, float scale,
+                                void* stream) {
+  if (!q || !k || !v || !o || !dout || !lse || !dq || !dk || !dv) return ATTN_ERR_NULLPTR;
+  int st = check_shape(B, N, Hq, Hkv, d);
+  if (st != ATTN_OK) return st;
+  // the GQA head split only where its partials fit beside D
+  const bool split = attn::bwd_workspace_layout(B, N, Hq, Hkv, d, true).total <= kNoAllocScratch;
+  if (!split && attn::bwd_workspace_layout(B, N, Hq, Hkv, d, false).total > kNoAllocScratch)
+    return ATTN_ERR_SCRATCH;
+  st = check_device();
+  if (st != ATTN_OK) return st;
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != ATTN_OK) return st;
+  return bwd_common(7, nullptr, 0, N, 0, q, k, v, o, dout, lse, dq, dk, dv, ws, kNoAllocScratch, B, N, Hq,
+                    Hkv, d, dtype, causal, scale, stream, split);
+}
 
 // ---- standard (materialising) attention ----
 
@@ -467,6 +531,8 @@ const char* attn_strerror(int status) {
     case ATTN_ERR_DEVICE: return "no current HIP device, or it is not gfx950";
     case ATTN_ERR_HIP: return "a HIP launch failed";
     case ATTN_ERR_TOO_LARGE: return "sizes exceed the supported index range";
+    case ATTN_ERR_SCRATCH:
+      return "sizes need more device scratch than attn_bwd_noalloc holds (ATTN_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

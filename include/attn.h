@@ -30,7 +30,9 @@
  *
  * Ownership and ordering.  All buffers are owned by the caller.  The library
  * never allocates or frees device memory and keeps no state besides a
- * per-device property cache and a thread-local last-HIP-error code.  Work is
+ * per-device property cache, a thread-local last-HIP-error code and the
+ * static device scratch of attn_bwd_noalloc (a fixed array in the library's
+ * code object, present on every device the library runs on).  Work is
  * enqueued on `stream` (a hipStream_t; NULL means the legacy default stream)
  * and calls return without synchronising; the caller keeps every buffer alive
  * until the stream has finished.  Outputs must not alias inputs.  Calls that
@@ -69,8 +71,10 @@ typedef enum {
   ATTN_ERR_WORKSPACE = 7, /* workspace NULL or smaller than attn_bwd_workspace_bytes() */
   ATTN_ERR_DEVICE = 8,    /* no current HIP device, or it is not gfx950 */
   ATTN_ERR_HIP = 9,       /* a HIP launch failed; see attn_last_hip_error() */
-  ATTN_ERR_TOO_LARGE = 10 /* a tensor has 2^31 or more elements per (batch, head) slice,
-                             or the launch grid would exceed the device limits */
+  ATTN_ERR_TOO_LARGE = 10, /* a tensor has 2^31 or more elements per (batch, head) slice,
+                              or the launch grid would exceed the device limits */
+  ATTN_ERR_SCRATCH = 11    /* attn_bwd_noalloc: the sizes need more scratch than its static
+                              array holds (ATTN_NOALLOC_SCRATCH_BYTES) */
 } attn_status_t;
 
 /*
@@ -120,6 +124,30 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              const float* lse, void* dq, void* dk, void* dv, void* workspace,
              size_t workspace_bytes, int B, int N, int Hq, int Hkv, int d, int dtype,
              int causal, float scale, void* stream);
+
+/*
+ * attn_bwd without a workspace argument and without any device allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments (minus the workspace), result and validation as attn_bwd; its
+ * scratch -- D, and the float32 dK/dV partials of a split GQA group when they
+ * fit beside it (otherwise the group runs unsplit, the same result up to the
+ * order of float32 sums) -- lives in a static device array of
+ * ATTN_NOALLOC_SCRATCH_BYTES that every device the library runs on holds
+ * until the process ends.  Sizes whose D (4 * B * Hq * N bytes, plus
+ * alignment) does not fit return ATTN_ERR_SCRATCH before anything is
+ * launched.  No hipMalloc, hipFree or allocating library routine is called
+ * (the array's device address is looked up once per device, on the first
+ * call there).  All calls on one device share the array and nothing in it
+ * needs to start at zero (each call writes every value it reads): calls that
+ * overlap on one device -- on different streams or from different threads --
+ * race, and must be ordered by the caller.
+ */
+#define ATTN_NOALLOC_SCRATCH_BYTES 67108864 /* 64 MiB */
+
+int attn_bwd_noalloc(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                     const float* lse, void* dq, void* dk, void* dv, int B, int N, int Hq, int Hkv,
+                     int d, int dtype, int causal, float scale, void* stream);
 
 /*
  * The three stages attn_bwd runs, exposed so a caller can schedule or time
