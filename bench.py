@@ -773,16 +773,18 @@ def _read_csv(path):
 PROFILE_TAG = "B4_N4096_H16_d128"  # the benchmark workload, for profile file names
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
-    """Turn rocprofv3 CSV output of `bench.py` runs into profiles/ summaries.
+EVIDENCE_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_LDS_BANK_CONFLICT",
+                     "SQ_LDS_IDX_ACTIVE", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_TRANS_F32",
+                     "GRBM_GUI_ACTIVE")
 
-    trace_dir: a --kernel-trace --stats run (kernel_stats.csv); fetch_dir /
-    write_dir: --pmc FETCH_SIZE and --pmc WRITE_SIZE runs; evidence_dir: a
-    --pmc run of SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
-    SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE (or None).
-    Writes profiles/step_kernels_<workload>.txt (per-kernel time, HBM bytes,
-    MFMA busy, LDS conflicts) and profiles/bwd_dkdv_traffic_<workload>.json
-    (the dominant kernel's HBM bytes per launch, read back by the benchmark).
+
+def _profile_table(trace_dir, fetch_dir, write_dir, evidence_dir):
+    """Per-kernel rows from rocprofv3 CSV output: (header lines, rows, raw).
+
+    trace_dir: a --kernel-trace --stats run; fetch_dir / write_dir: --pmc
+    FETCH_SIZE and --pmc WRITE_SIZE runs whose program ran copy_calibration()
+    first; evidence_dir: a --pmc run of EVIDENCE_COUNTERS (any subset), or
+    None.  HBM bytes are the counters scaled by what they read for the copy.
     """
     import glob
 
@@ -805,10 +807,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
     stats = _read_csv(find(trace_dir, "*kernel_stats.csv"))
     fetch = per_kernel(fetch_dir, {"FETCH_SIZE"})
     write = per_kernel(write_dir, {"WRITE_SIZE"})
-    evid = per_kernel(evidence_dir, {"SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16",
-                                     "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE",
-                                     "GRBM_GUI_ACTIVE"}) if evidence_dir else {}
-
+    evid = per_kernel(evidence_dir, set(EVIDENCE_COUNTERS)) if evidence_dir else {}
     is_copy = lambda nm: "elementwise" in nm.lower() and "neg" in nm.lower()  # noqa: E731
     cname = next(k_ for k_ in fetch if is_copy(k_))
     cf, cw = fetch[cname]["FETCH_SIZE"], write[cname]["WRITE_SIZE"]
@@ -819,47 +818,122 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
         nm = nm.replace("(anonymous namespace)::", "").replace("attn::", "")
         return nm[nm.find("attn_"):nm.find("(")] if "attn_" in nm else nm[:60]
 
+    head = [f"HBM counter calibration: plain copy of {COPY_BYTES} B reads FETCH_SIZE {cf:.0f} KiB, "
+            f"WRITE_SIZE {cw:.0f} KiB -> byte scale {f_scale:.4f} (fetch) / {w_scale:.4f} (write)",
+            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
+            "MFMA FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512; co-exec = SQ_VALU_MFMA_COEXEC_CYCLES / "
+            "SQ_VALU_MFMA_BUSY_CYCLES (share of MFMA-busy cycles in which a VALU instruction also issued); "
+            "exp = SQ_INSTS_VALU_TRANS_F32 x 64 lanes",
+            "",
+            f"{'kernel':52s} {'calls':>5s} {'avg_us':>9s} {'pct':>6s} {'HBM_rd_MB':>10s} {'HBM_wr_MB':>10s} "
+            f"{'HBM_GB/s':>9s} {'MFMA_busy':>9s} {'MFMA_TFLOP':>10s} {'LDS_confl':>9s} {'co-exec':>8s} {'exp_G':>8s}"]
+    rows, raw = [], []
+    for r in stats:
+        nm = r["Name"]
+        if "attn_" not in nm:
+            continue
+        avg_us = float(r["AverageNs"]) / 1e3
+        fk = fetch.get(nm, {})
+        wk = write.get(nm, {})
+        ek = evid.get(nm, {})
+        rd = fk.get("FETCH_SIZE", float("nan")) * 1024.0 * f_scale
+        wr = wk.get("WRITE_SIZE", float("nan")) * 1024.0 * w_scale
+        gbs = (rd + wr) / (avg_us * 1e-6) / 1e9
+        nan = float("nan")
+        busy = ek["SQ_VALU_MFMA_BUSY_CYCLES"] * 8 / (ek["GRBM_GUI_ACTIVE"] * 1024.0) \
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in ek and "GRBM_GUI_ACTIVE" in ek else nan
+        tf = ek["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e12 if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in ek else nan
+        conf = ek["SQ_LDS_BANK_CONFLICT"] / max(1.0, ek["SQ_LDS_IDX_ACTIVE"]) \
+            if "SQ_LDS_BANK_CONFLICT" in ek and "SQ_LDS_IDX_ACTIVE" in ek else nan
+        coex = ek["SQ_VALU_MFMA_COEXEC_CYCLES"] / max(1.0, ek["SQ_VALU_MFMA_BUSY_CYCLES"]) \
+            if "SQ_VALU_MFMA_COEXEC_CYCLES" in ek and "SQ_VALU_MFMA_BUSY_CYCLES" in ek else nan
+        exps = ek["SQ_INSTS_VALU_TRANS_F32"] * 64 / 1e9 if "SQ_INSTS_VALU_TRANS_F32" in ek else nan
+        rows.append(f"{short(nm)[:52]:52s} {r['Calls']:>5s} {avg_us:9.2f} {float(r['Percentage']):6.2f} "
+                    f"{rd / 1e6:10.1f} {wr / 1e6:10.1f} {gbs:9.1f} {busy:9.3f} {tf:10.4f} {conf:9.4f} "
+                    f"{coex:8.3f} {exps:8.2f}")
+        raw.append((nm, rd, wr, fk.get("FETCH_SIZE"), wk.get("WRITE_SIZE"), avg_us, cf, cw))
+    return head, rows, raw
+
+
+def summarize_workload(trace_dir, fetch_dir, write_dir, evidence_dir, out_name, title, cmd):
+    """profiles/OUT_NAME from the four rocprofv3 runs of `bench.py
+    --profile-workload SPEC` (one workload per run)."""
+    head, rows, _ = _profile_table(trace_dir, fetch_dir, write_dir, evidence_dir)
+    lines = [title, ""] + [f"{k_ + ':':9s} {cmd.get(k_, '')}" for k_ in ("trace", "fetch", "write", "evidence")]
+    lines += [""] + head + rows
+    with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def profile_workload(spec: str, reps: int):
+    """Run one workload's forward and backward ``reps`` times each (after one
+    untimed call of each), for rocprofv3 counter passes."""
+    import numpy as np
+    import torch
+
+    import exact_io_aware_75_amd as ea
+
+    s = shape_of(spec)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    mk = lambda hh: torch.randn(s.b, s.n, hh, s.d, device=dev, generator=gen).to(torch.bfloat16)  # noqa: E731
+    q, k, v, do = mk(s.hq), mk(s.hkv), mk(s.hkv), mk(s.hq)
+    o, lse = torch.empty_like(q), torch.empty((s.b, s.hq, s.n), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(s.b, s.n, s.hq, s.hkv, s.d), dtype=torch.uint8, device=dev)
+    sc = 1.0 / float(np.sqrt(s.d))
+    for _ in range(1 + reps):
+        ea.attn_fwd(q, k, v, o, lse, s.causal, sc, stream)
+    for _ in range(1 + reps):
+        ea.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, ws, s.causal, sc, stream)
+    torch.cuda.synchronize()
+    print(f"profiled {spec}: {s}", flush=True)
+
+
+def shape_of(spec: str):
+    """A full-size workload by name: 'd:n:causal' (hidden-2048 layer), 'w256'
+    (MHA d = 256), 'gqa8' / 'gqa1' (GQA / MQA) or 'long32768' / 'long65536'."""
+    from exact_io_aware_75_amd import configs
+
+    if spec == "w256":
+        return configs.wide_head()
+    if spec.startswith("gqa"):
+        return configs.gqa(int(spec[3:]))
+    if spec.startswith("long"):
+        return configs.long_seq(int(spec[4:]))
+    d, n, c = spec.split(":")
+    return configs.hidden2048(int(d), int(n), c == "1")
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
+    """Turn rocprofv3 CSV output of `bench.py` runs into profiles/ summaries.
+
+    trace_dir: a --kernel-trace --stats run (kernel_stats.csv); fetch_dir /
+    write_dir: --pmc FETCH_SIZE and --pmc WRITE_SIZE runs; evidence_dir: a
+    --pmc run of SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16
+    SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE GRBM_GUI_ACTIVE (or None).
+    Writes profiles/step_kernels_<workload>.txt (per-kernel time, HBM bytes,
+    MFMA busy, LDS conflicts) and profiles/bwd_dkdv_traffic_<workload>.json
+    (the dominant kernel's HBM bytes per launch, read back by the benchmark).
+    """
+    head, rows, raw = _profile_table(trace_dir, fetch_dir, write_dir, evidence_dir)
     lines = [f"Kernels of one benchmark step (workload {PROFILE_TAG}, bf16; fwd + bwd, non-causal and causal)",
              "",
              f"trace:    {cmd.get('trace', '')}",
              f"fetch:    {cmd.get('fetch', '')}",
              f"write:    {cmd.get('write', '')}",
              f"evidence: {cmd.get('evidence', '')}",
-             "",
-             f"HBM counter calibration: plain copy of {COPY_BYTES} B reads FETCH_SIZE {cf:.0f} KiB, "
-             f"WRITE_SIZE {cw:.0f} KiB -> byte scale {f_scale:.4f} (fetch) / {w_scale:.4f} (write)",
-             "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs); "
-             "MFMA FLOP = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512",
-             "",
-             f"{'kernel':52s} {'calls':>5s} {'avg_us':>9s} {'pct':>6s} {'HBM_rd_MB':>10s} {'HBM_wr_MB':>10s} "
-             f"{'HBM_GB/s':>9s} {'MFMA_busy':>9s} {'MFMA_TFLOP':>10s} {'LDS_confl':>9s}"]
-    dom = None
-    for r in stats:
-        nm = r["Name"]
-        if "attn_" not in nm:
-            continue
-        avg_us = float(r["AverageNs"]) / 1e3
-        fk = next((v_ for k_, v_ in fetch.items() if k_ == nm), {})
-        wk = next((v_ for k_, v_ in write.items() if k_ == nm), {})
-        ek = next((v_ for k_, v_ in evid.items() if k_ == nm), {})
-        rd = fk.get("FETCH_SIZE", float("nan")) * 1024.0 * f_scale
-        wr = wk.get("WRITE_SIZE", float("nan")) * 1024.0 * w_scale
-        gbs = (rd + wr) / (avg_us * 1e-6) / 1e9
-        busy = conf = tf = float("nan")
-        if ek:
-            busy = ek["SQ_VALU_MFMA_BUSY_CYCLES"] * 8 / (ek["GRBM_GUI_ACTIVE"] * 1024.0)
-            tf = ek["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512 / 1e12
-            conf = ek["SQ_LDS_BANK_CONFLICT"] / max(1.0, ek["SQ_LDS_IDX_ACTIVE"])
-        lines.append(f"{short(nm)[:52]:52s} {r['Calls']:>5s} {avg_us:9.2f} {float(r['Percentage']):6.2f} "
-                     f"{rd / 1e6:10.1f} {wr / 1e6:10.1f} {gbs:9.1f} {busy:9.3f} {tf:10.4f} {conf:9.4f}")
-        if "attn_bwd_dkdv_kernel" in nm and ("128, false, false>" in nm or "Li128ELb0ELb0E" in nm):
-            dom = (nm, rd, wr, fk.get("FETCH_SIZE"), wk.get("WRITE_SIZE"), avg_us)
+             ""] + head + rows
+    dom = next((x for x in raw if "attn_bwd_dkdv_kernel" in x[0] and ("128, false, false>" in x[0])), None)
     if dom is None:
         raise SystemExit("dK/dV kernel (d=128, non-causal) not found in the trace")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", f"step_kernels_{PROFILE_TAG}.txt"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    nm, rd, wr, fkib, wkib, avg_us = dom
+    nm, rd, wr, fkib, wkib, avg_us, cf, cw = dom
     with open(TRAFFIC_FILE, "w") as f:
         json.dump({"kernel": nm, "source_sha256": kernel_source_hash(), "avg_us_rocprof": avg_us,
                    "fetch_kib": fkib, "write_kib": wkib, "copy_fetch_kib": cf, "copy_write_kib": cw,
@@ -956,6 +1030,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="CPU oracle baseline budget in seconds (0 disables it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-workload", metavar="SPEC",
+                    help="run one workload's fwd and bwd --steps times each for rocprofv3 counter passes and exit "
+                         "(SPEC: d:n:causal for the hidden-2048 layer, w256, gqa8, gqa1, long32768, long65536)")
+    ap.add_argument("--summarize-workload", nargs=6,
+                    metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "EVIDENCE_DIR", "OUT_NAME", "TITLE"),
+                    help="write per-kernel time, HBM bytes and counters of a --profile-workload run to "
+                         "profiles/OUT_NAME and exit")
     ap.add_argument("--oracle-sweep", action="store_true",
                     help="time the CPU fp64 oracle on every full-size workload (fwd, fwd+bwd) and exit")
     ap.add_argument("--no-targets", dest="targets", action="store_false",
@@ -979,6 +1060,9 @@ def main():
     if args.summarize:
         summarize_profiles(*args.summarize, json.loads(args.summarize_cmds))
         return
+    if args.summarize_workload:
+        summarize_workload(*args.summarize_workload, json.loads(args.summarize_cmds))
+        return
     if args.summarize_hbm:
         summarize_hbm(*args.summarize_hbm[:5], json.loads(args.summarize_cmds), args.summarize_hbm[5])
         return
@@ -992,6 +1076,11 @@ def main():
         sys.exit(2)
     if args.oracle_sweep:
         print(json.dumps({"oracle_sweep": oracle_sweep()}), flush=True)
+        return
+    if args.profile_workload:
+        if args.copy_calibration:
+            copy_calibration()
+        profile_workload(args.profile_workload, args.steps)
         return
     if args.no_cpu_baseline:
         args.cpu_seconds = 0.0

@@ -82,7 +82,12 @@ template <int D, bool CAUSAL, bool SPARSE = false, bool SPLIT = false, bool NARR
 // workgroups (the crossover measured on MI355X lies between 2048 and 4096 keys
 // at d = 128, between 8192 and 16384 at d = 64).
 template <int D> struct NarrowKeys { static constexpr int MAX = D == 64 ? 8192 : 2048; };
-constexpr float RESCALE_THRESHOLD = 8.0f;  // log2 units: rescale only if the max grows > 2^8
+// Reference max of the online softmax.  d = 128: it moves (and the
+// accumulators are rescaled) only when a lane's partial row sum over a tile
+// exceeds PSUM_LIMIT.  d = 64 and 256: when a tile's row max exceeds it by
+// more than RESCALE_THRESHOLD (log2 units).
+constexpr float PSUM_LIMIT = 65536.0f;
+constexpr float RESCALE_THRESHOLD = 8.0f;
 
 // Key-tile height per head dimension: every K or V tile is 16 KiB.
 template <int D> struct FwdTile { static constexpr int BN = 8192 / D; };
@@ -376,39 +381,58 @@ attn_fwd_kernel(FwdArgs a) {
     });
   };
 
-  // Softmax of the current tile's scores, split in pieces that fill the
-  // shadow of the next tile's score products: the row max over the first half
-  // of the k-steps, then the probabilities of the first half of the key
-  // k-steps over the second half.  The rest of P is formed inside P V.
+  // Softmax of the current tile's scores, formed in the shadow of the next
+  // tile's score products.  Two forms, by head dimension:
+  //  * d = 128 (MAX_FREE): no per-tile row max.  All of the tile's
+  //    probabilities are formed against the running reference max m_ref; if
+  //    every lane's partial row sums stay <= PSUM_LIMIT, every probability
+  //    does (no overflow, full relative precision) and the tile goes on to
+  //    P V.  Only a tile that exceeds it (or is infinite: a row's first tile,
+  //    m_ref = -inf, unless the prologue set it) takes the rare path that
+  //    moves m_ref to the tile's max, rescales what is accumulated and forms
+  //    the probabilities again.
+  //  * d = 64 and 256: the row max is formed over the first half of the next
+  //    tile's k-steps, the first half of P over the second half, and the rest
+  //    of P under the first P V products; m_ref moves only when the tile
+  //    raises it by more than 2^8 (RESCALE_THRESHOLD).  At d = 64 a tile's 64
+  //    probabilities per lane are too many for the score products' shadow
+  //    alone; at d = 256 (32 keys per tile) the split measured 1.6% faster.
+  constexpr bool MAX_FREE = D == 128;
   struct SoftState {
-    float mx4[4];
-    float nm;          // -(reference max the tile's P is scaled to)
-    float m_new;
-    bool need;         // wave-uniform: the reference max moves this tile
+    float mx4[4];      // row-max form: partial maxima
+    float nm;          // -(reference max the tile's P is formed against)
+    float m_new;       // row-max form: the reference max after this tile
+    bool need;         // row-max form, wave-uniform: the reference max moves
     float tsum[4];     // this tile's partial row sums
     uint32_t w[NKS][4];
   };
+  constexpr int PAIRS = NKS * 4;  // probability pairs per tile
 
   auto row_max_part = [&](const f32x16_t* s, SoftState& st, int e0, int e1) __attribute__((always_inline)) {
 #pragma unroll
-    for (int e = e0; e < e1; e += 2) {
+    for (int e = e0; e < e1; e += 2) {  // four max3 chains, two new scores per step
       const int sb = e / 16, r = e % 16;
-      st.mx4[(e >> 1) & 3] = fmaxf(st.mx4[(e >> 1) & 3], fmaxf(s[sb][r], s[sb][r + 1]));
+      const int a = (e >> 1) & 3;
+      st.mx4[a] = e < 8 ? fmaxf(s[sb][r], s[sb][r + 1]) : fmaxf(fmaxf(st.mx4[a], s[sb][r]), s[sb][r + 1]);
     }
   };
-  auto row_max_end = [&](SoftState& st) __attribute__((always_inline)) {
-    float mx = fmaxf(fmaxf(st.mx4[0], st.mx4[1]), fmaxf(st.mx4[2], st.mx4[3]));
+  // the tile's scaled row max (the two halves of a row meet across lanes l, l ^ 32)
+  auto row_max_scaled = [&](float mx) __attribute__((always_inline)) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, mx),
                                                      __builtin_bit_cast(uint32_t, mx), false, false);
     mx = fmaxf(__builtin_bit_cast(float, (uint32_t)sw[0]), __builtin_bit_cast(float, (uint32_t)sw[1]));
     // Causal, a row can have no allowed key in a tile (mx = -inf; with scale
-    // 0, -inf * 0 would be NaN, so the select keeps -inf) and no key at all so
-    // far (m_new = -inf; its probabilities are then shifted by 0, not +inf).
-    // Without a mask every tile gives every row a key.
-    const float mxs = (CAUSAL && mx == -INFINITY) ? -INFINITY : mx * c;
+    // 0, -inf * 0 would be NaN, so the select keeps -inf).  Without a mask
+    // every tile gives every row a key.
+    return (CAUSAL && mx == -INFINITY) ? -INFINITY : mx * c;
+  };
+  auto row_max_end = [&](SoftState& st) __attribute__((always_inline)) {
+    const float mxs = row_max_scaled(fmaxf(fmaxf(fmaxf(st.mx4[0], st.mx4[1]), st.mx4[2]), st.mx4[3]));
     // deferred rescale: move the reference max only when it grows by > 2^8
     st.need = __builtin_amdgcn_ballot_w64(mxs > m_ref + RESCALE_THRESHOLD) != 0;
     st.m_new = st.need ? fmaxf(m_ref, mxs) : m_ref;
+    // a row with no key so far keeps m_new = -inf; its probabilities are
+    // all masked, shifted by 0 rather than +inf
     st.nm = (CAUSAL && st.m_new == -INFINITY) ? 0.f : -st.m_new;
   };
   // probability pairs [p0, p1) of the tile, pair index = 4 * key-k-step + t
@@ -420,21 +444,33 @@ attn_fwd_kernel(FwdArgs a) {
       const int sb = f / 2, r = 8 * (f % 2) + 2 * t;
       float e0 = fast_exp2(__builtin_fmaf(s[sb][r], c, st.nm));
       float e1 = fast_exp2(__builtin_fmaf(s[sb][r + 1], c, st.nm));
-      if (MASK) {  // exp2(-inf * 0) would be NaN when scale == 0
+      if (MASK) {  // masked scores are -inf: -inf * c + nm is NaN at scale 0 (or nm = +inf)
         e0 = s[sb][r] == -INFINITY ? 0.f : e0;
         e1 = s[sb][r + 1] == -INFINITY ? 0.f : e1;
       }
       st.w[f][t] = pack2(Tag{}, e0, e1);
-      st.tsum[t] += e0 + e1;  // fp32 row sum: LSE must not carry 16-bit rounding
+      // fp32 row sums (LSE must not carry 16-bit rounding); the first pair
+      // of each slot starts them
+      if (pp < 4) st.tsum[t] = e0 + e1;
+      else st.tsum[t] += e0 + e1;
       asm volatile("" : "+v"(st.w[f][t]), "+v"(st.tsum[t]));  // formed here, not sunk to its use
     }
   };
-  auto soft_init = [&](SoftState& st) __attribute__((always_inline)) {
+  // max-free form, wave-uniform: some lane's partial row sums exceed PSUM_LIMIT
+  auto over_limit = [&](const SoftState& st) __attribute__((always_inline)) {
+    const float m = fmaxf(fmaxf(fmaxf(st.tsum[0], st.tsum[1]), st.tsum[2]), st.tsum[3]);
+    return __builtin_amdgcn_ballot_w64(m > PSUM_LIMIT) != 0;
+  };
+  // rescale what is accumulated by exp2(m_ref - m_new) and move m_ref (rare)
+  auto move_ref = [&](float m_new) __attribute__((always_inline)) {
+    // a lane whose row has seen no key yet keeps m_new = -inf: its factor is
+    // 1 (the accumulators are still zero), not exp2(-inf + inf) = NaN
+    const float alpha = (CAUSAL && m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - m_new);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      st.mx4[t] = -INFINITY;
-      st.tsum[t] = 0.f;
-    }
+    for (int t = 0; t < 4; ++t) lsum[t] *= alpha;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
+    m_ref = m_new;
   };
   auto apply_mask = [&](f32x16_t* s, int j) __attribute__((always_inline)) {
     const int key0 = ktile(j) * BN;
@@ -447,25 +483,12 @@ attn_fwd_kernel(FwdArgs a) {
         s[sb][r] = ok ? s[sb][r] : -INFINITY;
       }
   };
-  // move the reference max (rare) -- after the probabilities, before P V
-  auto rescale = [&](SoftState& st) __attribute__((always_inline)) {
-    if (st.need) {
-      // a lane whose row has seen no key yet keeps m_new = -inf: its factor
-      // is 1 (the accumulators are still zero), not exp2(-inf + inf) = NaN
-      const float alpha = (CAUSAL && st.m_new == -INFINITY) ? 1.f : fast_exp2(m_ref - st.m_new);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) lsum[t] *= alpha;
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) oacc[db] *= alpha;
-    }
-    m_ref = st.m_new;
-  };
-  // O^T += V^T P^T, the second half of P formed in the shadow of the first
-  // half's products; V^T fragments read PFV products ahead.
+  // O^T += V^T P^T; V^T fragments read PFV products ahead.  Row-max form:
+  // the second half of P formed in the shadow of the first half's products.
   auto pv = [&](const uint16_t* vs, const f32x16_t* s, SoftState& st, auto mask_tag) __attribute__((always_inline)) {
     constexpr int NF = NKS * NDB;
     constexpr int PFV = FwdPrefetch<D>::V;
-    constexpr int PAIRS2 = (NKS / 2) * 4;        // pairs still to form
+    constexpr int PAIRS2 = (NKS / 2) * 4;        // pairs still to form (row-max form)
     constexpr int NM2 = (NKS / 2) * NDB;         // products they may hide under
     frag8_t vf[PFV + 1];
     auto rd = [&](int f) __attribute__((always_inline)) {
@@ -480,33 +503,36 @@ attn_fwd_kernel(FwdArgs a) {
       constexpr int f = decltype(fc)::value;
       if constexpr (f + PFV < NF) vf[(f + PFV) % (PFV + 1)] = rd(f + PFV);
       constexpr int ks = f / NDB, db = f % NDB;
-      if constexpr (f < NM2) {  // pairs [PAIRS2 * f / NM2, PAIRS2 * (f + 1) / NM2) of the second half
+      if constexpr (!MAX_FREE && f < NM2) {  // pairs [PAIRS2 f / NM2, PAIRS2 (f + 1) / NM2) of the second half
         constexpr int q0 = PAIRS2 * f / NM2, q1 = PAIRS2 * (f + 1) / NM2;
         probs(s, st, (NKS / 2) * 4 + q0, (NKS / 2) * 4 + q1, mask_tag);
       }
       const u32x4_t wv = {st.w[ks][0], st.w[ks][1], st.w[ks][2], st.w[ks][3]};
       oacc[db] = mfma32(Tag{}, vf[f % (PFV + 1)], __builtin_bit_cast(frag8_t, wv), oacc[db]);
     });
+    if constexpr (!MAX_FREE) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) lsum[t] += st.tsum[t];
+      for (int t = 0; t < 4; ++t) lsum[t] += st.tsum[t];
+    }
   };
 
   // One pipelined step: softmax and P V of tile j (scores in s_cur) with the
   // next tile's scores formed in between.  HAS_NEXT false: no next scores.
   auto step = [&](int j, const uint16_t* knext, const uint16_t* vcur, f32x16_t* s_cur, f32x16_t* s_next,
                   auto mask_tag, auto next_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
     constexpr bool HAS_NEXT = decltype(next_tag)::value;
     SoftState st;
-    soft_init(st);
-    if (MASK) apply_mask(s_cur, j);
-    constexpr int H = NKK / 2 > 0 ? NKK / 2 : 1;   // k-steps for the row max
+    if constexpr (MAX_FREE) st.nm = -m_ref;
+    if (decltype(mask_tag)::value) apply_mask(s_cur, j);
+    constexpr int H = NKK / 2 > 0 ? NKK / 2 : 1;   // row-max form: k-steps for the row max
     constexpr int NE = NSB * 16;                   // score elements per lane
-    constexpr int PAIRS1 = (NKS / 2) * 4;          // probability pairs in the first half
+    constexpr int PAIRS1 = (NKS / 2) * 4;          // row-max form: pairs in the first half
     constexpr int H2 = NKK - H;                    // k-steps for them
     auto hook = [&](auto kkc) __attribute__((always_inline)) {
       constexpr int kk = decltype(kkc)::value;
-      if constexpr (kk < H) {
+      if constexpr (MAX_FREE) {
+        probs(s_cur, st, PAIRS * kk / NKK, PAIRS * (kk + 1) / NKK, mask_tag);
+      } else if constexpr (kk < H) {
         row_max_part(s_cur, st, NE * kk / H, NE * (kk + 1) / H);
         if constexpr (kk == H - 1) row_max_end(st);
       } else {
@@ -516,14 +542,29 @@ attn_fwd_kernel(FwdArgs a) {
     };
     if constexpr (HAS_NEXT) {
       // the next tile's products (this tile's softmax interleaved) issue at
-      // raised priority, ahead of the other wavefront on the SIMD (about 1%)
+      // raised priority, ahead of the other wavefront on the SIMD
       __builtin_amdgcn_s_setprio(1);
       scores(knext, s_next, hook);
       __builtin_amdgcn_s_setprio(0);
     } else {
       static_for<0, NKK>(hook);
     }
-    rescale(st);
+    if constexpr (MAX_FREE) {
+      if (over_limit(st)) {  // rare: move m_ref to the tile's max and form P again
+        float mx = -INFINITY;
+#pragma unroll
+        for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+          for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(s_cur[sb][r], s_cur[sb][r + 1]));
+        move_ref(fmaxf(m_ref, row_max_scaled(mx)));
+        st.nm = -m_ref;
+        probs(s_cur, st, 0, PAIRS, mask_tag);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) lsum[t] += st.tsum[t];
+    } else {
+      if (st.need) move_ref(st.m_new);
+    }
     pv(vcur, s_cur, st, mask_tag);
   };
 
@@ -540,6 +581,18 @@ attn_fwd_kernel(FwdArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   scores(kb0, sA, [](auto) {});
+  if constexpr (MAX_FREE) {
+    // the reference max starts at tile 0's row max when every row of the
+    // wavefront sees all of tile 0; otherwise the first check moves it
+    if (nfull > 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < NSB; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sA[sb][r], sA[sb][r + 1]));
+      m_ref = row_max_scaled(mx);
+    }
+  }
   __syncthreads();  // every wavefront is done with K_0 before K_2 replaces it
 
   // Iteration j: loads K_{j+2} -> K buffer j & 1 and V_{j+1} -> V buffer
