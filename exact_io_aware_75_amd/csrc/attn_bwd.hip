@@ -676,7 +676,11 @@ attn_bwd_dq_kernel(BwdArgs a) {
   }
   const size_t li = ((size_t)b * a.Hq + h) * a.N + qsafe;
   const float lse2 = a.lse[li] * 1.4426950408889634f;
-  const float dlt = a.delta[li];
+  // dP^T starts from -D (the same for every key of this lane's query), so
+  // the products leave dP - D; the first product reads it and writes other
+  // registers, so it is never copied
+  const float nd = -a.delta[li];
+  const f32x16_t negd = {nd, nd, nd, nd, nd, nd, nd, nd, nd, nd, nd, nd, nd, nd, nd, nd};
   const float c = a.scale_log2;  // scale * log2(e), signed
 
   const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.Nk * a.Hkv + g) * D;
@@ -726,7 +730,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
   auto tile = [&](int j, const uint16_t* ks, const uint16_t* vs, auto mask_tag)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    // Per 32-key sub-block: S^T = K Q^T and dP^T = V dO^T for this
+    // Per 32-key sub-block: S^T = K Q^T and dP^T - D = V dO^T - D for this
     // wavefront's 32 queries, then dS^T = P^T (dP^T - D) with
     // P^T = 2^(S^T c - LSE2); rows = keys 32 sb + 8 (r / 4) + 4 half + r % 4.
     const int key0 = MASK ? ktile(j) * BN : 0;
@@ -738,7 +742,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int sb = 0; sb < NSB; ++sb) {
       frag8_t dsf[2];
-      f32x16_t s = {}, dp = {};
+      f32x16_t s = {}, dp = negd;
       {  // K and V fragments of k-step kk + 1 are read while k-step kk's products run
         frag8_t ka[2], va[2];
         ka[0] = fr.row(ks, sb, 0);
@@ -767,7 +771,7 @@ attn_bwd_dq_kernel(BwdArgs a) {
             p0 = (32 * sb + 8 * (r >> 2) + (r & 3)) <= lim ? p0 : 0.f;
             p1 = (32 * sb + 8 * ((r + 1) >> 2) + ((r + 1) & 3)) <= lim ? p1 : 0.f;
           }
-          w[t] = pack2(Tag{}, p0 * (dp[r] - dlt), p1 * (dp[r + 1] - dlt));
+          w[t] = pack2(Tag{}, p0 * dp[r], p1 * dp[r + 1]);
         }
         const u32x4_t wv = {w[0], w[1], w[2], w[3]};
         dsf[hh] = __builtin_bit_cast(frag8_t, wv);
