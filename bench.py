@@ -860,7 +860,7 @@ def summarize_workload(trace_dir, fetch_dir, write_dir, evidence_dir, out_name, 
     --profile-workload SPEC` (one workload per run)."""
     head, rows, _ = _profile_table(trace_dir, fetch_dir, write_dir, evidence_dir)
     lines = [title, ""] + [f"{k_ + ':':9s} {cmd.get(k_, '')}" for k_ in ("trace", "fetch", "write", "evidence")]
-    lines += [""] + head + rows
+    lines += ["($R: the repository root; $O: an output directory; each command run from /tmp)", ""] + head + rows
     with open(os.path.join(ROOT, "profiles", out_name), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -926,6 +926,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
              f"fetch:    {cmd.get('fetch', '')}",
              f"write:    {cmd.get('write', '')}",
              f"evidence: {cmd.get('evidence', '')}",
+             "($R: the repository root; $O: an output directory; each command run from /tmp)",
              ""] + head + rows
     dom = next((x for x in raw if "attn_bwd_dkdv_kernel" in x[0] and ("128, false, false>" in x[0])), None)
     if dom is None:
