@@ -680,6 +680,22 @@ attn_fwd_kernel(FwdArgs a) {
         j += 2;
       }
     }
+    if constexpr (!CAUSAL && !SPLIT && !SPARSE) {
+      // non-causal, two tiles left after the steady state: the first
+      // (unmasked) still forms the last tile's scores under its softmax; only
+      // the last (masked where the sequence ends in it) runs unpipelined.
+      // (Block-sparse and split-KV leave them to the loop below: this block
+      // spills registers in the block-sparse kernel.)
+      if (j + 2 == ntiles && j < nfull) {
+        iter_loads(j, kb0, vb1);
+        step(j, kb1, vb0, sA, sB, std::false_type{}, std::true_type{});
+        iter_end();
+        iter_loads(j + 1, kb1, vb0);
+        step(j + 1, kb0, vb1, sB, sA, std::true_type{}, std::false_type{});
+        iter_end();
+        j += 2;
+      }
+    }
     // remaining tiles: the diagonal / ragged ones, the last unmasked ones, and
     // tiles only other wavefronts need (causal: at most this wavefront's last
     // tile is computed here, except at d = 64 when a causal offset leaves more
