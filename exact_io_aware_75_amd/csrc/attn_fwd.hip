@@ -6,19 +6,22 @@
 //    result is folded into the output (FlashAttention-2 announcement, "具体实现"
 //    section; FlashAttention-1 news page, "FlashAttention" section).
 //  * Parallel over sequence length: one workgroup per (batch, query head,
-//    block of 256 query rows, 128 when causal, at d = 256 or over short key
-//    sequences), so the grid fills 256 CUs even for small batch * heads
-//    (announcement, "具体实现"; review, "Параллелизм").
+//    block of 256 query rows; 128 at d = 256, causal at d = 64, over short
+//    key sequences, block-sparse and split-KV), so the grid fills 256 CUs
+//    even for small batch * heads (announcement, "具体实现"; review,
+//    "Параллелизм").
 //  * Work split inside a workgroup: each 64-lane wavefront owns 32 query rows
 //    and all wavefronts share the K/V tiles, so wavefronts never exchange
 //    partial outputs (announcement, "具体实现": Q split across warps, K/V
 //    shared).
 //  * Online softmax with the rescale deferred: the reference max only moves
-//    (and the accumulator is only rescaled) when a tile raises a row's max by
-//    more than 2^8 in the exp2 domain, and the single division by the row sum
-//    happens once in the epilogue -- fewer non-matmul operations without
-//    changing the output (announcement, "具体实现": the softmax trick
-//    rewritten to cut rescaling, bounds checks and causal masking).
+//    (and the accumulator is only rescaled) when it must -- at d = 128 when a
+//    tile's probabilities, formed against it, would sum past 2^16 in a lane;
+//    at d = 64 and 256 when a tile raises a row's max by more than 2^8 in the
+//    exp2 domain -- and the single division by the row sum happens once in
+//    the epilogue: fewer non-matmul operations without changing the output
+//    (announcement, "具体实现": the softmax trick rewritten to cut rescaling,
+//    bounds checks and causal masking).
 //  * Causal: key tiles wholly above the diagonal are never visited, and only
 //    tiles that cross the diagonal or the ragged end of the sequence run the
 //    element mask; the steady-state loop carries no mask code at all (review,
@@ -26,10 +29,9 @@
 //
 // CDNA4 mapping.
 //  * Occupancy: two wavefronts per SIMD (<= 256 registers each) at d <= 128:
-//    one workgroup of eight wavefronts per CU when non-causal, so a K/V tile
-//    staged in LDS serves 256 query rows, or two workgroups of four when
-//    causal or when the key sequence is short.  At d = 256 one wavefront per
-//    SIMD.
+//    one workgroup of eight wavefronts per CU, so a K/V tile staged in LDS
+//    serves 256 query rows, or two workgroups of four (causal at d = 64, short
+//    key sequences).  At d = 256 one wavefront per SIMD.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 //    accumulator holds one query per lane and 16 keys per register block, so
 //    the row max / row sum are in-lane except one v_permlane32_swap between
@@ -37,14 +39,13 @@
 //    O^T += V^T P^T.  V^T comes from the row-major V tile through
 //    ds_read_b64_tr_b16.  Q stays in registers for the whole loop.
 //  * Software pipeline inside each wavefront: while the matrix cores form
-//    the scores of key tile j + 1, the VALU reduces the row max of tile j and
-//    exponentiates the first half of its probabilities; the second half is
-//    exponentiated under the first half of tile j's P V products.  A single
-//    wavefront's VALU work thus issues in the shadow of its own MFMAs instead
-//    of waiting for the other wavefront on the SIMD.  Non-causal, the tiles
-//    after the last unmasked one (the ragged end) run unpipelined; causal,
-//    the masked tiles (the diagonal) are pipelined too and only each
-//    wavefront's last tile is not.
+//    the scores of key tile j + 1, the VALU forms the probabilities of tile j
+//    (d = 128: all of them; d = 64 and 256: its row max and the first half,
+//    the second half under the first half of tile j's P V products).  A
+//    single wavefront's VALU work thus issues in the shadow of its own MFMAs
+//    instead of waiting for the other wavefront on the SIMD.  Only each
+//    wavefront's last tile runs unpipelined (and, at the ragged end of a
+//    non-causal sequence, the tiles after the last two whole ones).
 //  * K/V tiles go HBM -> LDS by buffer_load_dwordx4 ... lds (no register
 //    staging) through a buffer resource whose record count ends at the last
 //    key: rows past the end of the sequence arrive as zeros, with no clamp
@@ -61,21 +62,22 @@ namespace attn {
 
 namespace {
 
-// Wavefronts per workgroup (32 query rows each).  Non-causal at d <= 128:
-// eight, one workgroup per CU at two wavefronts per SIMD, so each K/V tile is
-// staged once per 256 query rows -- except over short key sequences (the
-// SHORT instantiation, which the host picks up to NarrowKeys keys; causal,
-// SHORT pairs row blocks instead, FwdPaired), where each workgroup's loop is short
+// Wavefronts per workgroup (32 query rows each).  Dense d <= 128: eight,
+// one workgroup per CU at two wavefronts per SIMD, so each K/V tile is staged
+// once per 256 query rows -- except over short key sequences (the SHORT
+// instantiation, which the host picks up to NarrowKeys keys; causal, SHORT
+// pairs row blocks instead, FwdPaired), where each workgroup's loop is short
 // next to its fixed prologue and epilogue: there two workgroups of four per
 // CU, one in its loop while the other loads or stores, win over staging each
-// tile for more rows.  Causal: four, since the wavefronts of a
+// tile for more rows.  Causal d = 64: four, since the wavefronts of a
 // diagonal block have unequal trip counts and wait for the longest at every
-// barrier.  d = 256: four (one wavefront per SIMD).  Block-sparse: four, so
-// that a workgroup's 128 rows are one row of the block mask.  Split-KV: four,
-// since it serves short query sequences, where 256-row blocks would be
-// mostly past the end.
+// barrier; at d = 128 the halved staging outweighs that from 4096 rows on
+// (+2.5-3% at 8192-65536, even at 4096).  d = 256: four (one wavefront per
+// SIMD).  Block-sparse: four, so that a workgroup's 128 rows are one row of
+// the block mask.  Split-KV: four, since it serves short query sequences,
+// where 256-row blocks would be mostly past the end.
 template <int D, bool CAUSAL, bool SPARSE = false, bool SPLIT = false, bool SHORT = false> struct FwdWG {
-  static constexpr int WAVES = (D <= 128 && !CAUSAL && !SPARSE && !SPLIT && !SHORT) ? 8 : 4;
+  static constexpr int WAVES = (D <= 128 && !SPARSE && !SPLIT && !SHORT && (!CAUSAL || D == 128)) ? 8 : 4;
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BM = WAVES * 32;
 };
