@@ -226,14 +226,17 @@ template <int D> struct BwdOcc { static constexpr int WAVES_PER_SIMD = D <= 128 
 // pass at d <= 128 runs eight (one workgroup per CU at two wavefronts per
 // SIMD), so each staged K/V tile serves 256 queries: 5-8% faster than four.
 // Causal dQ keeps four (the wavefronts of a diagonal block have unequal trip
-// counts), and so does dK/dV, where eight measured 3% slower non-causal and
-// 14% slower causal (a 256-key block computes more masked diagonal tiles).
+// counts) except at d = 128 from DQ_WIDE_ROWS query rows on (the WIDE
+// instantiation: +1-2% there, up to 9% slower over short sequences), and
+// dK/dV keeps four, where eight measured 3% slower non-causal and 14% slower
+// causal (a 256-key block computes more masked diagonal tiles).
 // Block-sparse dQ keeps four too, so that a workgroup's 128 queries are one
 // row of the block mask (as a dK/dV workgroup's 128 keys are one column).
 template <int D, bool CAUSAL> struct DkdvWG { static constexpr int WAVES = 4; };
-template <int D, bool CAUSAL, bool SPARSE = false> struct DqWG {
-  static constexpr int WAVES = (D <= 128 && !CAUSAL && !SPARSE) ? 8 : 4;
+template <int D, bool CAUSAL, bool SPARSE = false, bool WIDE = false> struct DqWG {
+  static constexpr int WAVES = (D <= 128 && !SPARSE && (!CAUSAL || WIDE)) ? 8 : 4;
 };
+constexpr int DQ_WIDE_ROWS = 8192;
 template <int D, int W> struct BwdBounds {
   static constexpr int THREADS = 64 * W;
   static constexpr int MIN_WG = BwdOcc<D>::WAVES_PER_SIMD * 4 / W;
@@ -579,11 +582,11 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
 // 32-key tiles run the d = 128 dQ pass 18% faster.)
 template <int D> struct DqTile { static constexpr int BN = D == 64 ? 128 : 32; };
 
-template <typename Tag, int D, bool CAUSAL, bool SPARSE>
-__global__ void __launch_bounds__((BwdBounds<D, DqWG<D, CAUSAL, SPARSE>::WAVES>::THREADS),
-                                  (BwdBounds<D, DqWG<D, CAUSAL, SPARSE>::WAVES>::MIN_WG))
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool WIDE = false>
+__global__ void __launch_bounds__((BwdBounds<D, DqWG<D, CAUSAL, SPARSE, WIDE>::WAVES>::THREADS),
+                                  (BwdBounds<D, DqWG<D, CAUSAL, SPARSE, WIDE>::WAVES>::MIN_WG))
 attn_bwd_dq_kernel(BwdArgs a) {
-  constexpr int W = DqWG<D, CAUSAL, SPARSE>::WAVES;
+  constexpr int W = DqWG<D, CAUSAL, SPARSE, WIDE>::WAVES;
   constexpr int DQ_BM = 32 * W;  // queries per workgroup
   constexpr int BN = DqTile<D>::BN;  // keys per tile
   constexpr int TILE = BN * D;
@@ -860,6 +863,17 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_reduce_kernel(BwdArgs a) {
   *(u32x2_t*)((uint16_t*)a.dv + i) = (u32x2_t){pack2(Tag{}, sv[0], sv[1]), pack2(Tag{}, sv[2], sv[3])};
 }
 
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool WIDE>
+hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
+  constexpr int W = DqWG<D, CAUSAL, SPARSE, WIDE>::WAVES;
+  const long long grid = (long long)((a.N + 32 * W - 1) / (32 * W)) * a.Hq * a.B;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const void* kfn = reinterpret_cast<const void*>(&attn_bwd_dq_kernel<Tag, D, CAUSAL, SPARSE, WIDE>);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL, SPARSE, WIDE>), dim3((unsigned)grid), dim3(64 * W),
+                     one_wg_lds_pad(kfn, a.lt.one_wg_per_cu), stream, a);
+  return hipGetLastError();
+}
+
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   if (SPARSE && (a.sp.bmask == nullptr || a.sp.nb != (a.N + SPARSE_BLOCK - 1) / SPARSE_BLOCK ||
@@ -896,13 +910,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     }
   }
   if (stages & 4) {
-    constexpr int W = DqWG<D, CAUSAL, SPARSE>::WAVES;
-    const long long grid = (long long)((a.N + 32 * W - 1) / (32 * W)) * a.Hq * a.B;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const void* kfn = reinterpret_cast<const void*>(&attn_bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>);
-    hipLaunchKernelGGL((attn_bwd_dq_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W),
-                       one_wg_lds_pad(kfn, a.lt.one_wg_per_cu), stream, a);
-    return hipGetLastError();
+    if constexpr (CAUSAL && !SPARSE && D == 128) {
+      if (a.N >= DQ_WIDE_ROWS) return launch_dq<Tag, D, CAUSAL, SPARSE, true>(a, stream);
+    }
+    return launch_dq<Tag, D, CAUSAL, SPARSE, false>(a, stream);
   }
   return hipSuccess;
 }
