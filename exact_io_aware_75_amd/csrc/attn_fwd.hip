@@ -15,9 +15,9 @@
 //    partial outputs (announcement, "具体实现": Q split across warps, K/V
 //    shared).
 //  * Online softmax with the rescale deferred: the reference max only moves
-//    (and the accumulator is only rescaled) when it must -- at d = 128 when a
-//    tile's probabilities, formed against it, would sum past 2^16 in a lane;
-//    at d = 64 and 256 when a tile raises a row's max by more than 2^8 in the
+//    (and the accumulator is only rescaled) when it must -- at d <= 128 when
+//    a tile's probabilities, formed against it, would sum past 2^16 in a
+//    lane; at d = 256 when a tile raises a row's max by more than 2^8 in the
 //    exp2 domain -- and the single division by the row sum happens once in
 //    the epilogue: fewer non-matmul operations without changing the output
 //    (announcement, "具体实现": the softmax trick rewritten to cut rescaling,
@@ -31,7 +31,8 @@
 //  * Occupancy: two wavefronts per SIMD (<= 256 registers each) at d <= 128:
 //    one workgroup of eight wavefronts per CU, so a K/V tile staged in LDS
 //    serves 256 query rows, or two workgroups of four (causal at d = 64, short
-//    key sequences).  At d = 256 one wavefront per SIMD.
+//    key sequences; three over short key sequences at d = 64, non-causal).
+//    At d = 256 one wavefront per SIMD.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16: the
 //    accumulator holds one query per lane and 16 keys per register block, so
 //    the row max / row sum are in-lane except one v_permlane32_swap between
@@ -40,8 +41,8 @@
 //    ds_read_b64_tr_b16.  Q stays in registers for the whole loop.
 //  * Software pipeline inside each wavefront: while the matrix cores form
 //    the scores of key tile j + 1, the VALU forms the probabilities of tile j
-//    (d = 128: all of them; d = 64 and 256: its row max and the first half,
-//    the second half under the first half of tile j's P V products).  A
+//    (d <= 128: all of them; d = 256: its row max and the first half, the
+//    second half under the first half of tile j's P V products).  A
 //    single wavefront's VALU work thus issues in the shadow of its own MFMAs
 //    instead of waiting for the other wavefront on the SIMD.  Only each
 //    wavefront's last tile runs unpipelined (and, at the ragged end of a
@@ -71,8 +72,8 @@ namespace {
 // CU, one in its loop while the other loads or stores, win over staging each
 // tile for more rows.  Causal d = 64: four, since the wavefronts of a
 // diagonal block have unequal trip counts and wait for the longest at every
-// barrier; at d = 128 the halved staging outweighs that from 4096 rows on
-// (+2.5-3% at 8192-65536, even at 4096).  d = 256: four (one wavefront per
+// barrier (eight: 3% slower at 4096 rows); at d = 128 the halved staging
+// outweighs that from 4096 rows on (+2.5-3% at 8192-65536, even at 4096).  d = 256: four (one wavefront per
 // SIMD).  Block-sparse: four, so that a workgroup's 128 rows are one row of
 // the block mask.  Split-KV: four, since it serves short query sequences,
 // where 256-row blocks would be mostly past the end.
@@ -81,28 +82,32 @@ template <int D, bool CAUSAL, bool SPARSE = false, bool SPLIT = false, bool SHOR
   static constexpr int THREADS = WAVES * 64;
   static constexpr int BM = WAVES * 32;
 };
-// Dense causal launches at d = 128 over short sequences (at most
+// Dense causal launches at d <= 128 over short sequences (at most
 // PAIRED_MAX_BLOCKS row blocks; the SHORT instantiation) pair row blocks of
 // complementary weight in one workgroup.  Longer sequences keep the
-// weight-major order, which measured 0.5-1% faster there; d = 64 spills
-// registers over the pass loop.
+// weight-major order, which measured 0.5-1% faster there.
 template <bool CAUSAL, bool SPARSE, bool SPLIT, bool SHORT> struct FwdPaired {
   static constexpr bool value = CAUSAL && !SPARSE && !SPLIT && SHORT;
 };
 constexpr int PAIRED_MAX_BLOCKS = 16;
 // Key count up to which the non-causal dense forward runs four-wavefront
 // workgroups (the crossover measured on MI355X lies between 2048 and 4096 keys
-// at d = 128, between 8192 and 16384 at d = 64).
-template <int D> struct NarrowKeys { static constexpr int MAX = D == 64 ? 8192 : 2048; };
-// Reference max of the online softmax.  d = 128: it moves (and the
+// at d = 128; at d = 64, with three wavefronts per SIMD, they were still 4.4%
+// faster at 16384, the longest measured).
+template <int D> struct NarrowKeys { static constexpr int MAX = D == 64 ? 16384 : 2048; };
+// Reference max of the online softmax.  d <= 128: it moves (and the
 // accumulators are rescaled) only when a lane's partial row sum over a tile
-// exceeds PSUM_LIMIT.  d = 64 and 256: when a tile's row max exceeds it by
-// more than RESCALE_THRESHOLD (log2 units).
+// exceeds PSUM_LIMIT.  d = 256: when a tile's row max exceeds it by more than
+// RESCALE_THRESHOLD (log2 units).
 constexpr float PSUM_LIMIT = 65536.0f;
 constexpr float RESCALE_THRESHOLD = 8.0f;
 
-// Key-tile height per head dimension: every K or V tile is 16 KiB.
-template <int D> struct FwdTile { static constexpr int BN = 8192 / D; };
+// Key-tile height per head dimension: 64 keys at d <= 128 (8 KiB K or V tiles
+// at d = 64, 16 KiB at d = 128), 32 at d = 256 (16 KiB).  At d = 64, 128-key
+// tiles would double the score registers of the pipeline (two tiles' worth
+// live at once), which left no room for the row-max-free softmax and cost
+// 4-10% there.
+template <int D> struct FwdTile { static constexpr int BN = D == 256 ? 32 : 64; };
 
 // 16-byte-chunk swizzles of the LDS tiles (row r, logical chunk c is stored at
 // chunk c ^ swz(r)); LDS has 64 four-byte banks, i.e. 16 chunk-wide bank groups.
@@ -122,8 +127,10 @@ typedef __attribute__((address_space(3))) void* lptr_t;
 
 // Wavefronts per SIMD the register budget is cut for: two for d <= 128; at
 // d = 256 the resident Q (64 registers) and O^T (128) leave too little for two.
+// The four-wavefront non-causal kernel at d = 64 fits three (168 registers,
+// with K fragments read one k-step ahead): +3-10% over two at N <= 16384.
 template <int D, bool CAUSAL, bool SPARSE, bool SPLIT, bool SHORT> struct FwdOcc {
-  static constexpr int WAVES_PER_SIMD = D <= 128 ? 2 : 1;
+  static constexpr int WAVES_PER_SIMD = (D == 64 && SHORT && !CAUSAL) ? 3 : D <= 128 ? 2 : 1;
   static constexpr int MIN_WG_PER_CU =
       WAVES_PER_SIMD * 4 / FwdWG<D, CAUSAL, SPARSE, SPLIT, SHORT>::WAVES;  // launch-bounds form
 };
@@ -137,8 +144,8 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 // How far ahead the LDS operand reads run: K fragments in k-steps of the score
-// product (three at d = 256, whose 16 k-steps per tile leave more room),
-// V^T fragments in products of P V.
+// product (three at d = 256, whose 16 k-steps per tile leave more room; one in
+// the three-wavefront-per-SIMD kernel), V^T fragments in products of P V.
 template <int D> struct FwdPrefetch {
   static constexpr int K = D == 256 ? 3 : 2;
   static constexpr int V = 2;
@@ -159,7 +166,7 @@ attn_fwd_kernel(FwdArgs a) {
   constexpr int NSB = BN / 32;          // 32-key sub-blocks per tile
   constexpr int NDB = D / 32;           // 32-wide d blocks of O
   constexpr int NKS = BN / 16;          // k-steps over keys in P V
-  static_assert(TILE == 8192 && LPT * 8 * WG::THREADS == TILE, "tile shape");
+  static_assert(LPT * 8 * WG::THREADS == TILE, "tile shape");
   constexpr int TPB = SPARSE_BLOCK / BN;  // key tiles per block of the mask
   static_assert(!SPARSE || FWD_BM == SPARSE_BLOCK, "one workgroup per row of the block mask");
   constexpr bool PAIRED = FwdPaired<CAUSAL, SPARSE, SPLIT, SHORT>::value;
@@ -391,7 +398,8 @@ attn_fwd_kernel(FwdArgs a) {
     // hook(kk) places independent VALU work after k-step kk's products, so that
     // it issues while they run.
     auto scores = [&](const uint16_t* ks, f32x16_t* s, auto&& hook) __attribute__((always_inline)) {
-      constexpr int PF = FwdPrefetch<D>::K < NKK ? FwdPrefetch<D>::K : NKK;
+      constexpr int PFK = FwdOcc<D, CAUSAL, SPARSE, SPLIT, SHORT>::WAVES_PER_SIMD == 3 ? 1 : FwdPrefetch<D>::K;
+      constexpr int PF = PFK < NKK ? PFK : NKK;
       frag8_t kf[PF + 1][NSB];
   #pragma unroll
       for (int sb = 0; sb < NSB; ++sb) s[sb] = (f32x16_t){};
@@ -414,7 +422,7 @@ attn_fwd_kernel(FwdArgs a) {
 
     // Softmax of the current tile's scores, formed in the shadow of the next
     // tile's score products.  Two forms, by head dimension:
-    //  * d = 128 (MAX_FREE): no per-tile row max.  All of the tile's
+    //  * d <= 128 (MAX_FREE): no per-tile row max.  All of the tile's
     //    probabilities are formed against the running reference max m_ref; if
     //    every lane's partial row sums stay <= PSUM_LIMIT, every probability
     //    does (no overflow, full relative precision) and the tile goes on to
@@ -422,13 +430,12 @@ attn_fwd_kernel(FwdArgs a) {
     //    m_ref = -inf, unless the prologue set it) takes the rare path that
     //    moves m_ref to the tile's max, rescales what is accumulated and forms
     //    the probabilities again.
-    //  * d = 64 and 256: the row max is formed over the first half of the next
+    //  * d = 256: the row max is formed over the first half of the next
     //    tile's k-steps, the first half of P over the second half, and the rest
     //    of P under the first P V products; m_ref moves only when the tile
-    //    raises it by more than 2^8 (RESCALE_THRESHOLD).  At d = 64 a tile's 64
-    //    probabilities per lane are too many for the score products' shadow
-    //    alone; at d = 256 (32 keys per tile) the split measured 1.6% faster.
-    constexpr bool MAX_FREE = D == 128;
+    //    raises it by more than 2^8 (RESCALE_THRESHOLD).  (At 32 keys per
+    //    tile this split measured 1.6% faster than the MAX_FREE form.)
+    constexpr bool MAX_FREE = D <= 128;
     struct SoftState {
       float mx4[4];      // row-max form: partial maxima
       float nm;          // -(reference max the tile's P is formed against)
@@ -638,15 +645,9 @@ attn_fwd_kernel(FwdArgs a) {
       __syncthreads();
     };
     int j = 0;
-    // steady state: tiles j and j + 1 unmasked, tile j + 2 computed by this
-    // wavefront (its scores are formed here, its mask applied when its turn
-    // comes) and, except causal at d = 64, unmasked too.  At d = 64 a causal
-    // wavefront's only masked tile is its last, so the loop runs up to it and
-    // the two-tile block below takes the rest.  (Where that does not pay -- d >=
-    // 128, which has its own masked loop, and split-KV -- the stricter bound
-    // keeps the kernels free of register spills.)
-    constexpr bool UP_TO_LAST = CAUSAL && D == 64 && !SPLIT;
-    for (; UP_TO_LAST ? (j + 2 <= nfull && j + 2 < nwave) : (j + 2 < nfull); j += 2) {
+    // steady state: tiles j, j + 1 and j + 2 unmasked (tile j + 2's scores
+    // are formed here)
+    for (; j + 2 < nfull; j += 2) {
       iter_loads(j, kb0, vb1);
       step(j, kb1, vb0, sA, sB, std::false_type{}, std::true_type{});
       iter_end();
@@ -654,25 +655,21 @@ attn_fwd_kernel(FwdArgs a) {
       step(j + 1, kb0, vb1, sB, sA, std::false_type{}, std::true_type{});
       iter_end();
     }
-    if constexpr (CAUSAL && (D >= 128 || UP_TO_LAST)) {
+    if constexpr (CAUSAL) {
       // the tiles up to this wavefront's last one (the diagonal and the ragged
       // end among them), pipelined like the steady state with the element mask
-      // on; j is even here, so the buffers alternate as above.  At d = 64 (one
-      // masked 128-key tile per wavefront) only the last two tiles take this
-      // path: a second pair of masked tile bodies spills registers there.
-      if constexpr (D >= 128) {
-        for (; j + 2 < nwave; j += 2) {
-          iter_loads(j, kb0, vb1);
-          step(j, kb1, vb0, sA, sB, std::true_type{}, std::true_type{});
-          iter_end();
-          iter_loads(j + 1, kb1, vb0);
-          step(j + 1, kb0, vb1, sB, sA, std::true_type{}, std::true_type{});
-          iter_end();
-        }
+      // on; j is even here, so the buffers alternate as above
+      for (; j + 2 < nwave; j += 2) {
+        iter_loads(j, kb0, vb1);
+        step(j, kb1, vb0, sA, sB, std::true_type{}, std::true_type{});
+        iter_end();
+        iter_loads(j + 1, kb1, vb0);
+        step(j + 1, kb0, vb1, sB, sA, std::true_type{}, std::true_type{});
+        iter_end();
       }
-      // two tiles left (at d >= 128 the loop above leaves at most two): the
-      // first pipelined, the last's scores in sB
-      if (D >= 128 ? j + 1 < nwave : j + 2 == nwave) {
+      // two tiles left (the loop above leaves at most two): the first
+      // pipelined, the last's scores in sB
+      if (j + 1 < nwave) {
         iter_loads(j, kb0, vb1);
         step(j, kb1, vb0, sA, sB, std::true_type{}, std::true_type{});
         iter_end();
@@ -698,11 +695,9 @@ attn_fwd_kernel(FwdArgs a) {
         j += 2;
       }
     }
-    // remaining tiles: the diagonal / ragged ones, the last unmasked ones, and
-    // tiles only other wavefronts need (causal: at most this wavefront's last
-    // tile is computed here, except at d = 64 when a causal offset leaves more
-    // than two tiles after the unmasked ones, and for causal split-KV at
-    // d = 64).  Not overlapped: the next tile's scores are formed after
+    // remaining tiles: the ragged ones, the last unmasked ones, and tiles only
+    // other wavefronts need (causal: at most this wavefront's last tile is
+    // computed here).  Not overlapped: the next tile's scores are formed after
     // this one's P V, in the same registers.
     for (; j < ntiles; ++j) {
       uint16_t* kcur = (j & 1) ? kb1 : kb0;   // K buffer j & 1 receives K_{j+2}
@@ -849,7 +844,7 @@ hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
   if constexpr (!CAUSAL && D <= 128) {
     if (a.Nk <= NarrowKeys<D>::MAX) return launch_fwd_s<Tag, D, false, false, false, true>(a, stream);
   }
-  if constexpr (CAUSAL && D == 128) {
+  if constexpr (CAUSAL && D <= 128) {
     if ((a.N + 127) / 128 <= PAIRED_MAX_BLOCKS) return launch_fwd_s<Tag, D, true, false, false, true>(a, stream);
   }
   return launch_fwd_s<Tag, D, CAUSAL, false, false>(a, stream);
