@@ -50,6 +50,14 @@ namespace attn {
 
 namespace {
 
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 typedef __attribute__((address_space(1))) const void* gptr_t;
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void* lptr_t;
@@ -730,6 +738,87 @@ attn_bwd_dq_kernel(BwdArgs a) {
     dma.load(vbase + off, a.Nk - kt * BN, kv_row, vs);
   };
 
+  // Several 32-key sub-blocks per tile (d = 64): software-pipelined, the
+  // S^T / dP^T products of sub-block sb + 1 issuing while the dS of sub-block
+  // sb forms, then sub-block sb's dQ products.
+  auto tile_pipe = [&](int j, const uint16_t* ks, const uint16_t* vs, auto mask_tag)
+      __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int key0 = MASK ? ktile(j) * BN : 0;
+    int lim = 0;
+    if (MASK) {
+      lim = a.Nk - 1 - key0 - 4 * half;
+      if (CAUSAL) lim = min(lim, qrow + a.coff - key0 - 4 * half);
+    }
+    f32x16_t sx[2], dpx[2];
+    // S^T, dP^T - D of sub-block sb into s, dp; hook(kk) after k-step kk
+    auto prod_a = [&](auto sbc, f32x16_t& s, f32x16_t& dp, auto&& hook) __attribute__((always_inline)) {
+      constexpr int sb = decltype(sbc)::value;
+      s = (f32x16_t){};
+      dp = negd;
+      frag8_t ka[2], va[2];
+      ka[0] = fr.row(ks, sb, 0);
+      va[0] = fr.row(vs, sb, 0);
+      static_for<0, NKK>([&](auto kkc) __attribute__((always_inline)) {
+        constexpr int kk = decltype(kkc)::value;
+        if constexpr (kk + 1 < NKK) {
+          ka[(kk + 1) & 1] = fr.row(ks, sb, kk + 1);
+          va[(kk + 1) & 1] = fr.row(vs, sb, kk + 1);
+        }
+        s = mfma32(Tag{}, ka[kk & 1], qf[kk], s);
+        dp = mfma32(Tag{}, va[kk & 1], of[kk], dp);
+        hook(kkc);
+      });
+    };
+    // dS pair t (elements r = 8 (t / 4) + 2 (t % 4), r + 1) of sub-block sb
+    auto ds_pair = [&](auto sbc, const f32x16_t& s, const f32x16_t& dp, int t, uint32_t* w)
+        __attribute__((always_inline)) {
+      constexpr int sb = decltype(sbc)::value;
+      const int r = 8 * (t >> 2) + 2 * (t & 3);
+      float p0 = fast_exp2(__builtin_fmaf(s[r], c, -lse2));
+      float p1 = fast_exp2(__builtin_fmaf(s[r + 1], c, -lse2));
+      if (MASK) {
+        p0 = (32 * sb + 8 * (r >> 2) + (r & 3)) <= lim ? p0 : 0.f;
+        p1 = (32 * sb + 8 * ((r + 1) >> 2) + ((r + 1) & 3)) <= lim ? p1 : 0.f;
+      }
+      w[t] = pack2(Tag{}, p0 * dp[r], p1 * dp[r + 1]);
+      asm volatile("" : "+v"(w[t]));  // formed here, under the products
+    };
+    auto prod_c = [&](auto sbc, const frag8_t* dsf) __attribute__((always_inline)) {
+      constexpr int sb = decltype(sbc)::value;
+      constexpr int NF = 2 * NDB;
+      constexpr int PFT = 2;
+      frag8_t ta[PFT + 1];
+#pragma unroll
+      for (int f = 0; f < PFT; ++f) ta[f] = fr.tr(ks, 2 * sb + f / NDB, f % NDB);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        if (f + PFT < NF) ta[(f + PFT) % (PFT + 1)] = fr.tr(ks, 2 * sb + (f + PFT) / NDB, (f + PFT) % NDB);
+        dq_acc[f % NDB] = mfma32(Tag{}, ta[f % (PFT + 1)], dsf[f / NDB], dq_acc[f % NDB]);
+      }
+    };
+    prod_a(std::integral_constant<int, 0>{}, sx[0], dpx[0], [](auto) {});
+    static_for<0, NSB>([&](auto sbc) __attribute__((always_inline)) {
+      constexpr int sb = decltype(sbc)::value;
+      uint32_t w[8];
+      if constexpr (sb + 1 < NSB) {
+        constexpr int PER = 8 / NKK;  // dS pairs per k-step of the next products
+        prod_a(std::integral_constant<int, sb + 1>{}, sx[(sb + 1) & 1], dpx[(sb + 1) & 1],
+               [&](auto kkc) __attribute__((always_inline)) {
+                 constexpr int kk = decltype(kkc)::value;
+#pragma unroll
+                 for (int t = PER * kk; t < PER * (kk + 1); ++t) ds_pair(sbc, sx[sb & 1], dpx[sb & 1], t, w);
+               });
+      } else {
+#pragma unroll
+        for (int t = 0; t < 8; ++t) ds_pair(sbc, sx[sb & 1], dpx[sb & 1], t, w);
+      }
+      const frag8_t dsf[2] = {__builtin_bit_cast(frag8_t, (u32x4_t){w[0], w[1], w[2], w[3]}),
+                              __builtin_bit_cast(frag8_t, (u32x4_t){w[4], w[5], w[6], w[7]})};
+      prod_c(sbc, dsf);
+    });
+  };
+
   auto tile = [&](int j, const uint16_t* ks, const uint16_t* vs, auto mask_tag)
       __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -809,8 +898,13 @@ attn_bwd_dq_kernel(BwdArgs a) {
       else load(j + 1, k1s, v1s);
     }
     if (!MASK || j < nwave) {
-      if (buf) tile(j, k1s, v1s, mask_tag);
-      else tile(j, k0s, v0s, mask_tag);
+      if constexpr (NSB > 1) {
+        if (buf) tile_pipe(j, k1s, v1s, mask_tag);
+        else tile_pipe(j, k0s, v0s, mask_tag);
+      } else {
+        if (buf) tile(j, k1s, v1s, mask_tag);
+        else tile(j, k0s, v0s, mask_tag);
+      }
     }
     wait_loads();
     barrier_lds();
