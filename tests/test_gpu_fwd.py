@@ -62,15 +62,42 @@ def test_small_shapes(gpu_device, b, n, hq, hkv, d, dtype, causal):
 
 
 # Non-causal forwards run four-wavefront workgroups up to 2048 keys at d = 128
-# and 8192 at d = 64, eight beyond; these sit just past those key counts, so
-# the eight-wavefront path (ragged last tile included) is checked on every
-# element too, not only on the sampled rows of the full-size workloads.
+# (two per CU) and 16384 at d = 64 (three wavefronts per SIMD), eight beyond.
+# The d = 128 case sits just past its threshold, so the eight-wavefront path
+# (ragged last tile included) is checked on every element; the d = 64 case
+# checks the three-per-SIMD kernel at a ragged length on every element.
 @pytest.mark.parametrize("b,n,hq,hkv,d,dtype", [(1, 2100, 2, 1, 128, "bf16"), (1, 8250, 1, 1, 64, "fp16")])
 def test_eight_wavefront_path(gpu_device, b, n, hq, hkv, d, dtype):
     x = gen.make_inputs(b, n, hq, hkv, d, dtype, cfg_id=7, seed=n, with_do=False)
     scale = 1.0 / np.sqrt(d)
     o, lse = run_fwd(x, dtype, False, scale, gpu_device)
     _check_full(x, o, lse, False, scale, f"b{b} n{n} hq{hq} hkv{hkv} d{d} {dtype} non-causal", dtype)
+
+
+# The eight-wavefront d = 64 forward (more than 16384 keys, non-causal):
+# sampled rows against the oracle, the ragged end and the block edges among them.
+def test_eight_wavefront_path_d64_long(gpu_device):
+    b, n, hq, hkv, d, dtype = 1, 16500, 2, 1, 64, "fp16"
+    x = gen.make_inputs(b, n, hq, hkv, d, dtype, cfg_id=8, seed=n, with_do=False)
+    scale = 1.0 / np.sqrt(d)
+    o, lse = run_fwd(x, dtype, False, scale, gpu_device)
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+    rows = [0, 1, 255, 256, 16383, 16384, 16447, 16448, n - 2, n - 1] + list(range(5000, 16500, 1277))
+    go, ro_, gl, rl_ = [], [], [], []
+    for h in range(hq):
+        g = oracle.kv_head_of(h, hq, hkv)
+        ro, rl = oracle.attention_head_fwd(x["q"][0, :, h], x["k"][0, :, g], x["v"][0, :, g], False, scale,
+                                           rows=rows)
+        go.append(o[0, rows, h])
+        ro_.append(ro)
+        gl.append(lse[0, h, rows])
+        rl_.append(rl)
+    go, ro_, gl, rl_ = np.concatenate(go), np.concatenate(ro_), np.concatenate(gl), np.concatenate(rl_)
+    tag = f"b{b} n{n} hq{hq} hkv{hkv} d{d} {dtype} non-causal rows={len(gl)}"
+    worst_o, _ = record(tag, "o", go, ro_, TOL_O, dtype)
+    worst_l, _ = record(tag, "lse", gl, rl_, TOL_LSE)
+    log(f"{tag}: max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+    assert excess(go, ro_, TOL_O, dtype) <= 0 and worst_l <= TOL_LSE
 
 
 @pytest.mark.parametrize("scale", [0.0, -0.09, 0.5])

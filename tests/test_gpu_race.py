@@ -28,7 +28,8 @@ CASES = [
     (2, 1000, 4, 2, 128, "bf16", True),
     (2, 1000, 4, 2, 128, "bf16", False),
     (1, 2100, 2, 1, 128, "bf16", False),   # eight-wavefront forward, ragged end
-    (1, 8250, 1, 1, 64, "fp16", False),    # eight-wavefront forward at d = 64
+    (1, 8250, 1, 1, 64, "fp16", False),    # three wavefronts per SIMD (d = 64, short keys)
+    (1, 16500, 1, 1, 64, "fp16", False),   # eight-wavefront forward at d = 64
     (1, 8250, 2, 1, 128, "bf16", True),    # eight-wavefront causal forward and dQ at d = 128
     (1, 512, 8, 1, 64, "bf16", True),      # MQA: dK/dV head split + reduce
     (1, 777, 8, 2, 128, "bf16", False),    # GQA head split, non-causal
