@@ -168,3 +168,33 @@ def test_full_size(gpu_device, s):
     log(f"  K/V head (b={bi}, g={g}, {len(cols)} keys): max|ddK|={ek:.3e} max|ddV|={ev:.3e} (bound {tkv:.3f})")
     assert excess(dk[bi, cols, g], rdk, tkv, s.dtype) <= 0
     assert excess(dv[bi, cols, g], rdv, tkv, s.dtype) <= 0
+
+
+# The stage entry points, enqueued in order (the last two either way round),
+# are exactly attn_bwd.
+@pytest.mark.parametrize("causal", [False, True])
+def test_stages_match_whole_pass(gpu_device, causal):
+    import torch
+    import exact_io_aware_75_amd as ea
+
+    b, n, hq, hkv, d = 2, 700, 4, 2, 128
+    x = gen.make_inputs(b, n, hq, hkv, d, "bf16", cfg_id=61, seed=n)
+    q, k, v, do = (gen.to_torch(x[t], "bf16", gpu_device) for t in ("q", "k", "v", "do"))
+    scale = 1.0 / np.sqrt(d)
+    o, lse = ea.forward(q, k, v, causal=causal, scale=scale)
+    ws = torch.empty(ea.attn_bwd_workspace_bytes(b, n, hq, hkv, d), dtype=torch.uint8, device=gpu_device)
+
+    def run(stages):
+        g = [torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)]
+        for st in stages:
+            ea.attn_bwd(q, k, v, o, do, lse, *g, ws, causal, scale, stage=st)
+        torch.cuda.synchronize()
+        return [t.float().cpu().numpy() for t in g]
+
+    whole = run(["attn_bwd"])
+    for order in (["attn_bwd_preprocess", "attn_bwd_dkdv", "attn_bwd_dq"],
+                  ["attn_bwd_preprocess", "attn_bwd_dq", "attn_bwd_dkdv"]):
+        staged = run(order)
+        for nm, a_, b_ in zip(("dq", "dk", "dv"), whole, staged):
+            assert np.array_equal(a_, b_), (order, nm)
+    log(f"stages causal={causal}: bitwise equal to attn_bwd in both orders")
