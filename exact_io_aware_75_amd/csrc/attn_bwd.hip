@@ -419,8 +419,9 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     else if (tid < 2 * KV_BM) ds[tid - KV_BM] = FOLD_D ? -lsd_raw : lsd_raw;
   };
 
-  // Causal: the mask is a branch-free select on every tile (cheap next to the
-  // 32 products of a tile), so one tile body serves all tiles.
+  // Causal: one tile body serves all tiles (a second full body spills); only
+  // the formation of P and dS takes the element mask, and at d >= 128 only
+  // on the tiles that cross the wavefront's diagonal.
   auto tile = [&](int q0, const uint16_t* qs, const uint16_t* os, const float* ls, const float* dls)
       __attribute__((always_inline)) {
     // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys;
@@ -463,24 +464,36 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
     // P = 2^(S c - LSE2), dS = P (dP - D)
     const int klim = mykey - a.coff - q0 - 4 * half;
     u32x4_t pq[2], dsq[2];  // packed P and dS, already the B-operand register tuples
+    auto form = [&](auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const f32x4_t l4 = *(const f32x4_t*)(ls + 8 * r4 + 4 * half);
-      f32x4_t d4 = {};
-      if (!FOLD_D) d4 = *(const f32x4_t*)(dls + 8 * r4 + 4 * half);
-      float p[4], dsv[4];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4_t l4 = *(const f32x4_t*)(ls + 8 * r4 + 4 * half);
+        f32x4_t d4 = {};
+        if (!FOLD_D) d4 = *(const f32x4_t*)(dls + 8 * r4 + 4 * half);
+        float p[4], dsv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * r4 + e;
-        float pv = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
-        if (CAUSAL) pv = (8 * r4 + e) < klim ? 0.f : pv;  // query < key
-        p[e] = pv;
-        dsv[e] = pv * (FOLD_D ? dp[r] : dp[r] - d4[e]);
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          float pv = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
+          if (MASK) pv = (8 * r4 + e) < klim ? 0.f : pv;  // query < key
+          p[e] = pv;
+          dsv[e] = pv * (FOLD_D ? dp[r] : dp[r] - d4[e]);
+        }
+        pq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, p[0], p[1]);
+        pq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, p[2], p[3]);
+        dsq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, dsv[0], dsv[1]);
+        dsq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, dsv[2], dsv[3]);
       }
-      pq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, p[0], p[1]);
-      pq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, p[2], p[3]);
-      dsq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, dsv[0], dsv[1]);
-      dsq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, dsv[2], dsv[3]);
+    };
+    // causal: only the tiles that cross this wavefront's diagonal (some lane
+    // has a query before its key) take the element mask -- at d >= 128; at
+    // d = 64 the second form would cost the three wavefronts per SIMD
+    if constexpr (CAUSAL && D >= 128) {
+      if (__builtin_amdgcn_ballot_w64(klim > 0) != 0) form(std::true_type{});
+      else form(std::false_type{});
+    } else {
+      form(std::bool_constant<CAUSAL>{});
     }
     // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries (two
     // k-steps); the transposed fragments are read PFT products ahead
