@@ -106,11 +106,12 @@ constexpr float RESCALE_THRESHOLD = 8.0f;
 // at d = 64, 16 KiB at d = 128), 32 at d = 256 (16 KiB).  At d = 64, 128-key
 // tiles would double the score registers of the pipeline (two tiles' worth
 // live at once), which left no room for the row-max-free softmax and cost
-// 4-10% there.  The paired short causal kernel at d = 128 (SMALL) takes 32-key
-// tiles: its passes are short and end on the diagonal, where the finer tiles
-// waste less (+3-4% at 1024 rows; 1-2% slower on long sequences).
+// 4-10% there.  The paired short causal kernel (SMALL) takes 32-key tiles:
+// its passes are short and end on the diagonal, where the finer tiles waste
+// less (d = 128: +2-7% at 512-2048 rows; d = 64: +7-15%; on long sequences
+// they were 1-2% slower).
 template <int D, bool SMALL = false> struct FwdTile {
-  static constexpr int BN = D == 256 || (SMALL && D == 128) ? 32 : 64;
+  static constexpr int BN = D == 256 || SMALL ? 32 : 64;
 };
 
 // 16-byte-chunk swizzles of the LDS tiles (row r, logical chunk c is stored at
