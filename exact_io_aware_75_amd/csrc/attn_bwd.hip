@@ -256,7 +256,7 @@ template <int D, int W> struct BwdBounds {
 constexpr int KV_BM = 32;   // query rows per tile
 constexpr int BWD_PFT = 2;  // transposed fragments read ahead in dV/dK
 
-template <typename Tag, int D, bool CAUSAL, bool SPARSE>
+template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool PAIRED = false>
 __global__ void __launch_bounds__((BwdBounds<D, DkdvWG<D, CAUSAL>::WAVES>::THREADS),
                                   (BwdBounds<D, DkdvWG<D, CAUSAL>::WAVES>::MIN_WG))
 attn_bwd_dkdv_kernel(BwdArgs a) {
@@ -294,303 +294,322 @@ attn_bwd_dkdv_kernel(BwdArgs a) {
   const int hs = D <= 128 ? a.hsplit : 1;
   const int nkb = (a.Nk + KV_BN - 1) / KV_BN;
   const int bid = grid_x(a.lt.reverse);
-  int bgs, kb;
-  if constexpr (CAUSAL && !SPARSE) {
+  int bgs, kb_first, kb_second = -1;
+  if constexpr (PAIRED) {
+    // Short causal sequences (at most PAIRED_MAX_BLOCKS key blocks): each
+    // workgroup takes key block p (the heavier) and then nkb - 1 - p, so all
+    // have the same work; the pairs of one (batch, kv head, head split) are
+    // consecutive work items on one XCD, which stream the same Q/dO tiles
+    // through its L2 at the same time.
+    const int npair = (nkb + 1) / 2;
+    const int L = xcd_remap(bid, npair * a.Hkv * a.B * hs);
+    bgs = L / npair;
+    kb_first = L - bgs * npair;
+    kb_second = nkb - 1 - kb_first != kb_first ? nkb - 1 - kb_first : -1;
+  } else if constexpr (CAUSAL && !SPARSE) {
     // Causal key blocks differ in work (the first sees every query):
     // weight-major order with consecutive work items on consecutive XCDs,
     // as in the causal forward pass.
     const int G = a.Hkv * a.B * hs;
-    kb = bid / G;
-    bgs = bid - kb * G;
+    kb_first = bid / G;
+    bgs = bid - kb_first * G;
   } else {
     const int Lw = xcd_remap(bid, nkb * a.Hkv * a.B * hs);
     bgs = Lw / nkb;
-    kb = Lw - bgs * nkb;
+    kb_first = Lw - bgs * nkb;
   }
-  const int bg = bgs / hs;
-  const int split = bgs - bg * hs;
-  const int gs = a.group / hs;  // query heads of the group this workgroup covers
-  const int b = bg / a.Hkv;
-  const int g = bg - b * a.Hkv;
-  const int k0 = kb * KV_BN;           // first key of the block
-  const int kw0 = k0 + wave * 32;      // first key of this wavefront
-  const int mykey = kw0 + l32;         // this lane's key (C-layout column)
+  // one key block, or (paired) two in turn; the LDS buffers are free between
+  // them, every loop step ending with a barrier
+  auto body = [&](const int kb) __attribute__((always_inline)) {
+    const int bg = bgs / hs;
+    const int split = bgs - bg * hs;
+    const int gs = a.group / hs;  // query heads of the group this workgroup covers
+    const int b = bg / a.Hkv;
+    const int g = bg - b * a.Hkv;
+    const int k0 = kb * KV_BN;           // first key of the block
+    const int kw0 = k0 + wave * 32;      // first key of this wavefront
+    const int mykey = kw0 + l32;         // this lane's key (C-layout column)
 
-  const int q_row = a.Hq * D;
-  const int kv_row = a.Hkv * D;
-  const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.Nk * a.Hkv + g) * D;
-  const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.Nk * a.Hkv + g) * D;
+    const int q_row = a.Hq * D;
+    const int kv_row = a.Hkv * D;
+    const uint16_t* kbase = (const uint16_t*)a.k + ((size_t)b * a.Nk * a.Hkv + g) * D;
+    const uint16_t* vbase = (const uint16_t*)a.v + ((size_t)b * a.Nk * a.Hkv + g) * D;
 
-  // K (and V if in registers) as B operands: lane = key, 8 consecutive d per k-step
-  frag8_t kf[NKK], vf[V_LDS ? 1 : NKK];
-  {
-    const uint16_t* kr = kbase + (size_t)min(mykey, a.Nk - 1) * kv_row + 8 * half;
-    const uint16_t* vr = vbase + (size_t)min(mykey, a.Nk - 1) * kv_row + 8 * half;
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      kf[kk] = *(const frag8_t*)(kr + 16 * kk);
-      if (!V_LDS) vf[V_LDS ? 0 : kk] = *(const frag8_t*)(vr + 16 * kk);
-    }
-  }
-  FragRd<D> fr;
-  fr.init(lane);
-  if (V_LDS) {  // the V block, [key][d], swizzled; read as B operand (lane = key)
-    TileDma<D, KV_BN, W> vdma;
-    vdma.init(kv_row, wave, lane);
-    vdma.load(vbase + (size_t)k0 * kv_row, a.Nk - k0, kv_row, vblk);
-  }
-
-  f32x16_t dk_acc[NDB], dv_acc[NDB];  // dK^T, dV^T: lane = key, rows = d
-#pragma unroll
-  for (int i = 0; i < NDB; ++i) {
-    dk_acc[i] = (f32x16_t){};
-    dv_acc[i] = (f32x16_t){};
-  }
-
-  // query tiles: every head of the GQA group x tiles of KV_BM rows
-  // (causal: only tiles with a row i that sees key k0, i + coff >= k0)
-  const int nqt = (a.N + KV_BM - 1) / KV_BM;
-  const int qt0 = CAUSAL ? min(nqt, max(0, floor_div(k0 - a.coff, KV_BM))) : 0;
-  int tiles_per_head = nqt - qt0;
-  // Block-sparse: the query tiles of the listed query blocks (causal: from
-  // the diagonal block on), KV_BM rows at a time; only the last block of the
-  // sequence can be ragged, and it can only be the last listed.
-  int nlist = 0;
-  if constexpr (SPARSE) {
-    if (wave == 0) {
-      const uint8_t* mcol = a.sp.bmask + (size_t)g * a.sp.mask_hstride + kb;
-      const int cnt = compact_mask(mcol, a.sp.nb, CAUSAL ? kb : 0, a.sp.nb, blist, lane);
-      if (lane == 0) bcount = cnt;
-    }
-    __syncthreads();
-    nlist = __builtin_amdgcn_readfirstlane(bcount);
-    constexpr int QPB = SPARSE_BLOCK / KV_BM;  // query tiles per block
-    tiles_per_head = nlist * QPB;
-    if (nlist > 0 && lds_uniform(blist, nlist - 1) == a.sp.nb - 1)
-      tiles_per_head -= QPB - (a.N - (a.sp.nb - 1) * SPARSE_BLOCK + KV_BM - 1) / KV_BM;
-  }
-  const int ntiles = tiles_per_head * gs;
-  const float c = a.scale_log2;  // scale * log2(e), signed
-
-  TileDma<D, KV_BM, W> qdma;
-  qdma.init(q_row, wave, lane);
-  // Tile coordinates advance incrementally: query rows within a head, then
-  // the next head of the group.
-  const int qfirst = qt0 * KV_BM, qend = nqt * KV_BM;
-  int li = 0;  // block-sparse: list entry of the next tile to load
-  auto advance = [&](int& h, int& q0) {
-    q0 += KV_BM;
-    if constexpr (SPARSE) {
-      const int blk = q0 - KV_BM - (q0 - KV_BM) % SPARSE_BLOCK;  // first row of the tile's block
-      if (q0 >= min(blk + SPARSE_BLOCK, a.N)) {
-        if (++li == nlist) {
-          li = 0;
-          ++h;
-        }
-        q0 = lds_uniform(blist, li) * SPARSE_BLOCK;
-      }
-    } else if (q0 >= qend) {
-      q0 = qfirst;
-      ++h;
-    }
-  };
-  // Q and dO tiles by DMA.  LSE and D of the tile's rows are loaded raw into
-  // a register by threads 0 .. 2 KV_BM - 1 (LSE by the first KV_BM, D by the
-  // rest) and only converted and stored to LDS at the end of the step, so
-  // nothing waits for the load before the tile's products.
-  float lsd_raw = 0.f;
-  bool lsd_valid = false;
-  auto load = [&](int h, int q0, uint16_t* qs, uint16_t* os) {
-    if (tid < 2 * KV_BM) {
-      const int qr = q0 + (tid & (KV_BM - 1));
-      const size_t li = ((size_t)b * a.Hq + h) * a.N + min(qr, a.N - 1);
-      const float* src = tid < KV_BM ? a.lse : a.delta;
-      lsd_raw = src[li];
-      lsd_valid = qr < a.N;
-    }
-    const size_t rowbase = ((size_t)b * a.N + q0) * a.Hq + h;
-    qdma.load((const uint16_t*)a.q + rowbase * D, a.N - q0, q_row, qs);
-    qdma.load((const uint16_t*)a.dout + rowbase * D, a.N - q0, q_row, os);
-  };
-  auto store_lsd = [&](float* ls, float* ds) {
-    // LSE in log2 units; rows past the end get +inf, so their probabilities
-    // are 0.  D is stored negated where it initialises the dP accumulator.
-    if (tid < KV_BM) ls[tid] = lsd_valid ? lsd_raw * 1.4426950408889634f : INFINITY;
-    else if (tid < 2 * KV_BM) ds[tid - KV_BM] = FOLD_D ? -lsd_raw : lsd_raw;
-  };
-
-  // Causal: one tile body serves all tiles (a second full body spills); only
-  // the formation of P and dS takes the element mask, and at d >= 128 only
-  // on the tiles that cross the wavefront's diagonal.
-  auto tile = [&](int q0, const uint16_t* qs, const uint16_t* os, const float* ls, const float* dls)
-      __attribute__((always_inline)) {
-    // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys;
-    // the Q, dO (and V) fragments of k-step kk + 1 are read while k-step kk's
-    // two products run
-    // At d <= 128 dP starts from -D (C rows = queries 8 (r / 4) + 4 half +
-    // r % 4, four consecutive rows per 128-bit read), so the products leave
-    // dP - D; at d = 256 (registers too tight) D is subtracted afterwards.
-    f32x16_t s = {}, dp = {};
-    if (FOLD_D) {
-      const f32x4_t n0 = *(const f32x4_t*)(dls + 4 * half), n1 = *(const f32x4_t*)(dls + 8 + 4 * half);
-      const f32x4_t n2 = *(const f32x4_t*)(dls + 16 + 4 * half), n3 = *(const f32x4_t*)(dls + 24 + 4 * half);
-      const f32x8_t lo = __builtin_shufflevector(n0, n1, 0, 1, 2, 3, 4, 5, 6, 7);
-      const f32x8_t hi = __builtin_shufflevector(n2, n3, 0, 1, 2, 3, 4, 5, 6, 7);
-      dp = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-    }
+    // K (and V if in registers) as B operands: lane = key, 8 consecutive d per k-step
+    frag8_t kf[NKK], vf[V_LDS ? 1 : NKK];
     {
-      frag8_t qa[2], oa[2], va[2];
-      auto rd = [&](int kk, int i) __attribute__((always_inline)) {
-        qa[i] = fr.row(qs, 0, kk);
-        oa[i] = fr.row(os, 0, kk);
-        if (V_LDS) va[i] = fr.row(vblk, wave, kk);
-      };
-      rd(0, 0);
-      // Issue priority: while a wavefront runs a block of products it issues
-      // ahead of the other wavefront on its SIMD, which meanwhile runs its
-      // exponentials; the matrix pipe then sees fewer gaps (3-4% on this pass).
-      __builtin_amdgcn_s_setprio(1);
+      const uint16_t* kr = kbase + (size_t)min(mykey, a.Nk - 1) * kv_row + 8 * half;
+      const uint16_t* vr = vbase + (size_t)min(mykey, a.Nk - 1) * kv_row + 8 * half;
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
-        if (kk + 1 < NKK) rd(kk + 1, (kk + 1) & 1);
-        s = mfma32(Tag{}, qa[kk & 1], kf[kk], s);
-        const frag8_t vv = V_LDS ? va[kk & 1] : vf[V_LDS ? 0 : kk];
-        dp = mfma32(Tag{}, oa[kk & 1], vv, dp);
-        if (kk + 1 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, V_LDS ? 3 : 2, 0);  // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                // MFMA
+        kf[kk] = *(const frag8_t*)(kr + 16 * kk);
+        if (!V_LDS) vf[V_LDS ? 0 : kk] = *(const frag8_t*)(vr + 16 * kk);
       }
-      __builtin_amdgcn_s_setprio(0);
     }
-    // P = 2^(S c - LSE2), dS = P (dP - D)
-    const int klim = mykey - a.coff - q0 - 4 * half;
-    u32x4_t pq[2], dsq[2];  // packed P and dS, already the B-operand register tuples
-    auto form = [&](auto mask_tag) __attribute__((always_inline)) {
-      constexpr bool MASK = decltype(mask_tag)::value;
+    FragRd<D> fr;
+    fr.init(lane);
+    if (V_LDS) {  // the V block, [key][d], swizzled; read as B operand (lane = key)
+      TileDma<D, KV_BN, W> vdma;
+      vdma.init(kv_row, wave, lane);
+      vdma.load(vbase + (size_t)k0 * kv_row, a.Nk - k0, kv_row, vblk);
+    }
+
+    f32x16_t dk_acc[NDB], dv_acc[NDB];  // dK^T, dV^T: lane = key, rows = d
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4_t l4 = *(const f32x4_t*)(ls + 8 * r4 + 4 * half);
-        f32x4_t d4 = {};
-        if (!FOLD_D) d4 = *(const f32x4_t*)(dls + 8 * r4 + 4 * half);
-        float p[4], dsv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          float pv = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
-          if (MASK) pv = (8 * r4 + e) < klim ? 0.f : pv;  // query < key
-          p[e] = pv;
-          dsv[e] = pv * (FOLD_D ? dp[r] : dp[r] - d4[e]);
+    for (int i = 0; i < NDB; ++i) {
+      dk_acc[i] = (f32x16_t){};
+      dv_acc[i] = (f32x16_t){};
+    }
+
+    // query tiles: every head of the GQA group x tiles of KV_BM rows
+    // (causal: only tiles with a row i that sees key k0, i + coff >= k0)
+    const int nqt = (a.N + KV_BM - 1) / KV_BM;
+    const int qt0 = CAUSAL ? min(nqt, max(0, floor_div(k0 - a.coff, KV_BM))) : 0;
+    int tiles_per_head = nqt - qt0;
+    // Block-sparse: the query tiles of the listed query blocks (causal: from
+    // the diagonal block on), KV_BM rows at a time; only the last block of the
+    // sequence can be ragged, and it can only be the last listed.
+    int nlist = 0;
+    if constexpr (SPARSE) {
+      if (wave == 0) {
+        const uint8_t* mcol = a.sp.bmask + (size_t)g * a.sp.mask_hstride + kb;
+        const int cnt = compact_mask(mcol, a.sp.nb, CAUSAL ? kb : 0, a.sp.nb, blist, lane);
+        if (lane == 0) bcount = cnt;
+      }
+      __syncthreads();
+      nlist = __builtin_amdgcn_readfirstlane(bcount);
+      constexpr int QPB = SPARSE_BLOCK / KV_BM;  // query tiles per block
+      tiles_per_head = nlist * QPB;
+      if (nlist > 0 && lds_uniform(blist, nlist - 1) == a.sp.nb - 1)
+        tiles_per_head -= QPB - (a.N - (a.sp.nb - 1) * SPARSE_BLOCK + KV_BM - 1) / KV_BM;
+    }
+    const int ntiles = tiles_per_head * gs;
+    const float c = a.scale_log2;  // scale * log2(e), signed
+
+    TileDma<D, KV_BM, W> qdma;
+    qdma.init(q_row, wave, lane);
+    // Tile coordinates advance incrementally: query rows within a head, then
+    // the next head of the group.
+    const int qfirst = qt0 * KV_BM, qend = nqt * KV_BM;
+    int li = 0;  // block-sparse: list entry of the next tile to load
+    auto advance = [&](int& h, int& q0) {
+      q0 += KV_BM;
+      if constexpr (SPARSE) {
+        const int blk = q0 - KV_BM - (q0 - KV_BM) % SPARSE_BLOCK;  // first row of the tile's block
+        if (q0 >= min(blk + SPARSE_BLOCK, a.N)) {
+          if (++li == nlist) {
+            li = 0;
+            ++h;
+          }
+          q0 = lds_uniform(blist, li) * SPARSE_BLOCK;
         }
-        pq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, p[0], p[1]);
-        pq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, p[2], p[3]);
-        dsq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, dsv[0], dsv[1]);
-        dsq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, dsv[2], dsv[3]);
+      } else if (q0 >= qend) {
+        q0 = qfirst;
+        ++h;
       }
     };
-    // causal: only the tiles that cross this wavefront's diagonal (some lane
-    // has a query before its key) take the element mask -- at d >= 128; at
-    // d = 64 the second form would cost the three wavefronts per SIMD
-    if constexpr (CAUSAL && D >= 128) {
-      if (__builtin_amdgcn_ballot_w64(klim > 0) != 0) form(std::true_type{});
-      else form(std::false_type{});
-    } else {
-      form(std::bool_constant<CAUSAL>{});
-    }
-    // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries (two
-    // k-steps); the transposed fragments are read PFT products ahead
-    {
-      constexpr int NF = 2 * 2 * NDB;  // products, in (ks, db, dV/dK) order
-      constexpr int PFT = BWD_PFT;
-      frag8_t ta[PFT + 1];
-      auto rd = [&](int f) __attribute__((always_inline)) {
-        const int ks = f / (2 * NDB), db = (f / 2) % NDB;
-        return fr.tr((f & 1) ? qs : os, ks, db);
-      };
-#pragma unroll
-      for (int f = 0; f < PFT; ++f) ta[f] = rd(f);
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        if (f + PFT < NF) ta[(f + PFT) % (PFT + 1)] = rd(f + PFT);
-        const int ks = f / (2 * NDB), db = (f / 2) % NDB;
-        if (f & 1)
-          dk_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, dsq[ks]), dk_acc[db]);
-        else
-          dv_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, pq[ks]), dv_acc[db]);
-        if (f + PFT < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+    // Q and dO tiles by DMA.  LSE and D of the tile's rows are loaded raw into
+    // a register by threads 0 .. 2 KV_BM - 1 (LSE by the first KV_BM, D by the
+    // rest) and only converted and stored to LDS at the end of the step, so
+    // nothing waits for the load before the tile's products.
+    float lsd_raw = 0.f;
+    bool lsd_valid = false;
+    auto load = [&](int h, int q0, uint16_t* qs, uint16_t* os) {
+      if (tid < 2 * KV_BM) {
+        const int qr = q0 + (tid & (KV_BM - 1));
+        const size_t li = ((size_t)b * a.Hq + h) * a.N + min(qr, a.N - 1);
+        const float* src = tid < KV_BM ? a.lse : a.delta;
+        lsd_raw = src[li];
+        lsd_valid = qr < a.N;
       }
-      __builtin_amdgcn_s_setprio(0);
-    }
-  };
+      const size_t rowbase = ((size_t)b * a.N + q0) * a.Hq + h;
+      qdma.load((const uint16_t*)a.q + rowbase * D, a.N - q0, q_row, qs);
+      qdma.load((const uint16_t*)a.dout + rowbase * D, a.N - q0, q_row, os);
+    };
+    auto store_lsd = [&](float* ls, float* ds) {
+      // LSE in log2 units; rows past the end get +inf, so their probabilities
+      // are 0.  D is stored negated where it initialises the dP accumulator.
+      if (tid < KV_BM) ls[tid] = lsd_valid ? lsd_raw * 1.4426950408889634f : INFINITY;
+      else if (tid < 2 * KV_BM) ds[tid - KV_BM] = FOLD_D ? -lsd_raw : lsd_raw;
+    };
 
-  // Tile t lives in buffer t & 1; one barrier per tile, the same number for
-  // every wavefront.
-  int lh = g * a.group + split * gs, lq = qfirst;  // coordinates of the next tile to load
-  if constexpr (SPARSE) lq = nlist > 0 ? lds_uniform(blist, 0) * SPARSE_BLOCK : 0;
-  if (ntiles > 0) {
-    load(lh, lq, q0s, o0s);
-    store_lsd(lse0, del0);
-  }
-  int cq = lq;  // first query row of the tile being computed
-  if (!SPARSE || ntiles > 0) advance(lh, lq);  // (an empty list has no entry to advance to)
-  wait_loads();
-  __syncthreads();
-  auto step = [&](int t, int buf) __attribute__((always_inline)) {
-    if (t + 1 < ntiles) {
-      if (buf) load(lh, lq, q0s, o0s);
-      else load(lh, lq, q1s, o1s);
+    // Causal: one tile body serves all tiles (a second full body spills); only
+    // the formation of P and dS takes the element mask, and at d >= 128 only
+    // on the tiles that cross the wavefront's diagonal.
+    auto tile = [&](int q0, const uint16_t* qs, const uint16_t* os, const float* ls, const float* dls)
+        __attribute__((always_inline)) {
+      // S = Q K^T and dP = dO V^T for 32 queries x this wavefront's 32 keys;
+      // the Q, dO (and V) fragments of k-step kk + 1 are read while k-step kk's
+      // two products run
+      // At d <= 128 dP starts from -D (C rows = queries 8 (r / 4) + 4 half +
+      // r % 4, four consecutive rows per 128-bit read), so the products leave
+      // dP - D; at d = 256 (registers too tight) D is subtracted afterwards.
+      f32x16_t s = {}, dp = {};
+      if (FOLD_D) {
+        const f32x4_t n0 = *(const f32x4_t*)(dls + 4 * half), n1 = *(const f32x4_t*)(dls + 8 + 4 * half);
+        const f32x4_t n2 = *(const f32x4_t*)(dls + 16 + 4 * half), n3 = *(const f32x4_t*)(dls + 24 + 4 * half);
+        const f32x8_t lo = __builtin_shufflevector(n0, n1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const f32x8_t hi = __builtin_shufflevector(n2, n3, 0, 1, 2, 3, 4, 5, 6, 7);
+        dp = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      }
+      {
+        frag8_t qa[2], oa[2], va[2];
+        auto rd = [&](int kk, int i) __attribute__((always_inline)) {
+          qa[i] = fr.row(qs, 0, kk);
+          oa[i] = fr.row(os, 0, kk);
+          if (V_LDS) va[i] = fr.row(vblk, wave, kk);
+        };
+        rd(0, 0);
+        // Issue priority: while a wavefront runs a block of products it issues
+        // ahead of the other wavefront on its SIMD, which meanwhile runs its
+        // exponentials; the matrix pipe then sees fewer gaps (3-4% on this pass).
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          if (kk + 1 < NKK) rd(kk + 1, (kk + 1) & 1);
+          s = mfma32(Tag{}, qa[kk & 1], kf[kk], s);
+          const frag8_t vv = V_LDS ? va[kk & 1] : vf[V_LDS ? 0 : kk];
+          dp = mfma32(Tag{}, oa[kk & 1], vv, dp);
+          if (kk + 1 < NKK) __builtin_amdgcn_sched_group_barrier(0x100, V_LDS ? 3 : 2, 0);  // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                // MFMA
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+      // P = 2^(S c - LSE2), dS = P (dP - D)
+      const int klim = mykey - a.coff - q0 - 4 * half;
+      u32x4_t pq[2], dsq[2];  // packed P and dS, already the B-operand register tuples
+      auto form = [&](auto mask_tag) __attribute__((always_inline)) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t l4 = *(const f32x4_t*)(ls + 8 * r4 + 4 * half);
+          f32x4_t d4 = {};
+          if (!FOLD_D) d4 = *(const f32x4_t*)(dls + 8 * r4 + 4 * half);
+          float p[4], dsv[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * r4 + e;
+            float pv = fast_exp2(__builtin_fmaf(s[r], c, -l4[e]));
+            if (MASK) pv = (8 * r4 + e) < klim ? 0.f : pv;  // query < key
+            p[e] = pv;
+            dsv[e] = pv * (FOLD_D ? dp[r] : dp[r] - d4[e]);
+          }
+          pq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, p[0], p[1]);
+          pq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, p[2], p[3]);
+          dsq[r4 >> 1][2 * (r4 & 1)] = pack2(Tag{}, dsv[0], dsv[1]);
+          dsq[r4 >> 1][2 * (r4 & 1) + 1] = pack2(Tag{}, dsv[2], dsv[3]);
+        }
+      };
+      // causal: only the tiles that cross this wavefront's diagonal (some lane
+      // has a query before its key) take the element mask -- at d >= 128; at
+      // d = 64 the second form would cost the three wavefronts per SIMD
+      if constexpr (CAUSAL && D >= 128) {
+        if (__builtin_amdgcn_ballot_w64(klim > 0) != 0) form(std::true_type{});
+        else form(std::false_type{});
+      } else {
+        form(std::bool_constant<CAUSAL>{});
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS over the tile's 32 queries (two
+      // k-steps); the transposed fragments are read PFT products ahead
+      {
+        constexpr int NF = 2 * 2 * NDB;  // products, in (ks, db, dV/dK) order
+        constexpr int PFT = BWD_PFT;
+        frag8_t ta[PFT + 1];
+        auto rd = [&](int f) __attribute__((always_inline)) {
+          const int ks = f / (2 * NDB), db = (f / 2) % NDB;
+          return fr.tr((f & 1) ? qs : os, ks, db);
+        };
+#pragma unroll
+        for (int f = 0; f < PFT; ++f) ta[f] = rd(f);
+        __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if (f + PFT < NF) ta[(f + PFT) % (PFT + 1)] = rd(f + PFT);
+          const int ks = f / (2 * NDB), db = (f / 2) % NDB;
+          if (f & 1)
+            dk_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, dsq[ks]), dk_acc[db]);
+          else
+            dv_acc[db] = mfma32(Tag{}, ta[f % (PFT + 1)], __builtin_bit_cast(frag8_t, pq[ks]), dv_acc[db]);
+          if (f + PFT < NF) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // DS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                    // MFMA
+        }
+        __builtin_amdgcn_s_setprio(0);
+      }
+    };
+
+    // Tile t lives in buffer t & 1; one barrier per tile, the same number for
+    // every wavefront.
+    int lh = g * a.group + split * gs, lq = qfirst;  // coordinates of the next tile to load
+    if constexpr (SPARSE) lq = nlist > 0 ? lds_uniform(blist, 0) * SPARSE_BLOCK : 0;
+    if (ntiles > 0) {
+      load(lh, lq, q0s, o0s);
+      store_lsd(lse0, del0);
     }
-    fr.pin();
-    if (buf) tile(cq, q1s, o1s, lse1, del1);
-    else tile(cq, q0s, o0s, lse0, del0);
-    cq = lq;
-    advance(lh, lq);
-    if (t + 1 < ntiles) {
-      if (buf) store_lsd(lse0, del0);
-      else store_lsd(lse1, del1);
-    }
+    int cq = lq;  // first query row of the tile being computed
+    if (!SPARSE || ntiles > 0) advance(lh, lq);  // (an empty list has no entry to advance to)
     wait_loads();
     __syncthreads();
-  };
-  int t = 0;
-  for (; t + 1 < ntiles; t += 2) {
-    step(t, 0);
-    step(t + 1, 1);
-  }
-  if (t < ntiles) step(t, 0);
+    auto step = [&](int t, int buf) __attribute__((always_inline)) {
+      if (t + 1 < ntiles) {
+        if (buf) load(lh, lq, q0s, o0s);
+        else load(lh, lq, q1s, o1s);
+      }
+      fr.pin();
+      if (buf) tile(cq, q1s, o1s, lse1, del1);
+      else tile(cq, q0s, o0s, lse0, del0);
+      cq = lq;
+      advance(lh, lq);
+      if (t + 1 < ntiles) {
+        if (buf) store_lsd(lse0, del0);
+        else store_lsd(lse1, del1);
+      }
+      wait_loads();
+      __syncthreads();
+    };
+    int t = 0;
+    for (; t + 1 < ntiles; t += 2) {
+      step(t, 0);
+      step(t + 1, 1);
+    }
+    if (t < ntiles) step(t, 0);
 
-  // ---- epilogue: dK = scale * dK_acc, dV = dV_acc; lane = key, rows = d ----
-  if (hs > 1) {  // fp32 partials of this head split, summed by the reduce kernel
-    if (mykey < a.Nk) {
-      const size_t per = (size_t)a.B * a.Nk * a.Hkv * D;
-      float* pk = a.dkv_part + (size_t)split * 2 * per + (((size_t)b * a.Nk + mykey) * a.Hkv + g) * D;
-      float* pv = pk + per;
+    // ---- epilogue: dK = scale * dK_acc, dV = dV_acc; lane = key, rows = d ----
+    if (hs > 1) {  // fp32 partials of this head split, summed by the reduce kernel
+      if (mykey < a.Nk) {
+        const size_t per = (size_t)a.B * a.Nk * a.Hkv * D;
+        float* pk = a.dkv_part + (size_t)split * 2 * per + (((size_t)b * a.Nk + mykey) * a.Hkv + g) * D;
+        float* pv = pk + per;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int d0 = 32 * db + 8 * q4 + 4 * half;
+            *(f32x4_t*)(pk + d0) = (f32x4_t){dk_acc[db][4 * q4], dk_acc[db][4 * q4 + 1], dk_acc[db][4 * q4 + 2],
+                                             dk_acc[db][4 * q4 + 3]};
+            *(f32x4_t*)(pv + d0) = (f32x4_t){dv_acc[db][4 * q4], dv_acc[db][4 * q4 + 1], dv_acc[db][4 * q4 + 2],
+                                             dv_acc[db][4 * q4 + 3]};
+          }
+      }
+    } else if (mykey < a.Nk) {
+      uint16_t* dkp = (uint16_t*)a.dk + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)mykey * kv_row;
+      uint16_t* dvp = (uint16_t*)a.dv + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)mykey * kv_row;
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int d0 = 32 * db + 8 * q4 + 4 * half;
-          *(f32x4_t*)(pk + d0) = (f32x4_t){dk_acc[db][4 * q4], dk_acc[db][4 * q4 + 1], dk_acc[db][4 * q4 + 2],
-                                           dk_acc[db][4 * q4 + 3]};
-          *(f32x4_t*)(pv + d0) = (f32x4_t){dv_acc[db][4 * q4], dv_acc[db][4 * q4 + 1], dv_acc[db][4 * q4 + 2],
-                                           dv_acc[db][4 * q4 + 3]};
+          const u32x2_t wk = {pack2(Tag{}, dk_acc[db][4 * q4] * a.scale, dk_acc[db][4 * q4 + 1] * a.scale),
+                              pack2(Tag{}, dk_acc[db][4 * q4 + 2] * a.scale, dk_acc[db][4 * q4 + 3] * a.scale)};
+          const u32x2_t wv = {pack2(Tag{}, dv_acc[db][4 * q4], dv_acc[db][4 * q4 + 1]),
+                              pack2(Tag{}, dv_acc[db][4 * q4 + 2], dv_acc[db][4 * q4 + 3])};
+          *(u32x2_t*)(dkp + d0) = wk;
+          *(u32x2_t*)(dvp + d0) = wv;
         }
     }
-  } else if (mykey < a.Nk) {
-    uint16_t* dkp = (uint16_t*)a.dk + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)mykey * kv_row;
-    uint16_t* dvp = (uint16_t*)a.dv + ((size_t)b * a.Nk * a.Hkv + g) * D + (size_t)mykey * kv_row;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int d0 = 32 * db + 8 * q4 + 4 * half;
-        const u32x2_t wk = {pack2(Tag{}, dk_acc[db][4 * q4] * a.scale, dk_acc[db][4 * q4 + 1] * a.scale),
-                            pack2(Tag{}, dk_acc[db][4 * q4 + 2] * a.scale, dk_acc[db][4 * q4 + 3] * a.scale)};
-        const u32x2_t wv = {pack2(Tag{}, dv_acc[db][4 * q4], dv_acc[db][4 * q4 + 1]),
-                            pack2(Tag{}, dv_acc[db][4 * q4 + 2], dv_acc[db][4 * q4 + 3])};
-        *(u32x2_t*)(dkp + d0) = wk;
-        *(u32x2_t*)(dvp + d0) = wv;
-      }
+  };
+  body(kb_first);
+  if constexpr (PAIRED) {
+    if (kb_second >= 0) body(kb_second);
   }
 }
 
@@ -981,6 +1000,13 @@ hipError_t launch_dq(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Dense causal dK/dV over short key sequences (at most PAIRED_MAX_BLOCKS blocks
+// of 128 keys) at d = 128: key blocks of complementary weight share a
+// workgroup (+3-16% on the backward at 512-2048 keys; at d = 64 the paired
+// kernel needs more registers than three wavefronts per SIMD allow and was
+// 3-8% slower).
+constexpr int PAIRED_MAX_BLOCKS = 16;
+
 template <typename Tag, int D, bool CAUSAL, bool SPARSE>
 hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
   if (SPARSE && (a.sp.bmask == nullptr || a.sp.nb != (a.N + SPARSE_BLOCK - 1) / SPARSE_BLOCK ||
@@ -1000,11 +1026,24 @@ hipError_t launch_bwd_t(const BwdArgs& a, int stages, hipStream_t stream) {
     if (a.hsplit < 1 || a.group % a.hsplit != 0 ||
         (a.hsplit > 1 && (SPARSE || D > 128 || a.dkv_part == nullptr)))
       return hipErrorInvalidValue;
-    const long long grid = (long long)((a.Nk + 32 * W - 1) / (32 * W)) * a.Hkv * a.B * a.hsplit;
+    const long long nkb = (a.Nk + 32 * W - 1) / (32 * W);
+    const long long grid = nkb * a.Hkv * a.B * a.hsplit;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    const void* kfn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>);
-    hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W),
-                       one_wg_lds_pad(kfn, a.lt.one_wg_per_cu), stream, a);
+    bool paired = false;
+    if constexpr (CAUSAL && !SPARSE && D == 128) {
+      if (nkb <= PAIRED_MAX_BLOCKS) {
+        paired = true;
+        const void* kfn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<Tag, D, true, false, true>);
+        hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, true, false, true>),
+                           dim3((unsigned)((nkb + 1) / 2 * a.Hkv * a.B * a.hsplit)), dim3(64 * W),
+                           one_wg_lds_pad(kfn, a.lt.one_wg_per_cu), stream, a);
+      }
+    }
+    if (!paired) {
+      const void* kfn = reinterpret_cast<const void*>(&attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>);
+      hipLaunchKernelGGL((attn_bwd_dkdv_kernel<Tag, D, CAUSAL, SPARSE>), dim3((unsigned)grid), dim3(64 * W),
+                         one_wg_lds_pad(kfn, a.lt.one_wg_per_cu), stream, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (a.hsplit > 1) {
