@@ -58,6 +58,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -934,7 +935,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, evidence_dir, cmd):
              f"evidence: {cmd.get('evidence', '')}",
              "($R: the repository root; $O: an output directory; each command run from /tmp)",
              ""] + head + rows
-    dom = next((x for x in raw if "attn_bwd_dkdv_kernel" in x[0] and ("128, false, false>" in x[0])), None)
+    # <dtype, d, causal, block-sparse, paired>
+    dom = next((x for x in raw if re.search(r"attn_bwd_dkdv_kernel<[^,<>]+, 128, false, false(, false)?>", x[0])), None)
     if dom is None:
         raise SystemExit("dK/dV kernel (d=128, non-causal) not found in the trace")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
