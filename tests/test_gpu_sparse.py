@@ -86,9 +86,9 @@ def test_small_shapes(gpu_device, b, n, hq, hkv, d, mh, dtype, causal):
     _check(x, out, mask, causal, scale, tag, dtype)
 
 
-@pytest.mark.parametrize("n,d", [(300, 64), (1000, 128), (520, 256)])
+@pytest.mark.parametrize("n,d", [(300, 64), (1000, 128), (520, 256), (2100, 64), (2100, 128)])
 @pytest.mark.parametrize("causal", [False, True])
-def test_full_mask_equals_dense_bitwise(gpu_device, n, d, causal):
+def test_full_mask_equals_dense(gpu_device, n, d, causal):
     x = gen.make_inputs(1, n, 4, 2, d, "bf16", cfg_id=32, seed=n)
     nb = -(-n // BLOCK)
     ones = np.ones((1, nb, nb), dtype=np.uint8)
@@ -104,18 +104,31 @@ def test_full_mask_equals_dense_bitwise(gpu_device, n, d, causal):
     # reordering error of its terms (bounded here by 1e-4 of the largest element,
     # 200x below the stated 2e-2 tolerance); everything else is bitwise equal.
     split = d <= 128
+    # The dense causal forward over at most 2048 rows (d <= 128) runs the paired
+    # short kernel, which steps 32 keys at a time; the block-sparse forward
+    # steps 64.  Its online softmax then rounds in another order, which the
+    # backward inherits through O and LSE: there the two paths are required to
+    # agree within the stated tolerances (each is checked against the oracle
+    # elsewhere).  The 2100-row cases take the same 64-key steps in both.
+    reorder = causal and d <= 128 and n <= 2048
+    tol = {"o": TOL_O, "lse": TOL_LSE}
     for name, u, w in zip(("o", "lse", "dq", "dk", "dv"), a, b):
-        if split and name in ("dk", "dv"):
+        if reorder or (split and name in ("dk", "dv")):
             diff = np.abs(u - w)
             i = np.unravel_index(np.argmax(diff), diff.shape)
             log(f"  {name}: max |sparse - dense| {diff[i]:.3e} at |dense| {abs(w[i]):.3e}")
-            assert np.all(diff <= 2.0 ** -7 * np.abs(w) + 1e-4 * np.abs(w).max()), name
+            if reorder:
+                assert diff.max() <= tol.get(name, TOL_GRAD), name
+            else:
+                assert np.all(diff <= 2.0 ** -7 * np.abs(w) + 1e-4 * np.abs(w).max()), name
         else:
             assert np.array_equal(u, w), name
 
 
 def test_lower_block_triangle_is_causal_bitwise(gpu_device):
-    n, d = 777, 128
+    # past 2048 rows, so the dense causal forward steps 64 keys at a time, as
+    # the block-sparse one does
+    n, d = 2100, 128
     x = gen.make_inputs(2, n, 4, 4, d, "bf16", cfg_id=33)
     nb = -(-n // BLOCK)
     tril = np.tril(np.ones((nb, nb), dtype=np.uint8))[None].repeat(4, axis=0)
