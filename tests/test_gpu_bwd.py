@@ -50,6 +50,7 @@ SMALL = [
     (1, 333, 8, 2, 256, "fp16"),
     (2, 256, 4, 1, 128, "bf16"),
     (1, 640, 2, 2, 64, "bf16"),
+    (1, 600, 2, 2, 128, "bf16"),   # five blocks of 128: the middle one unpaired, ragged end
 ]
 
 

@@ -35,6 +35,8 @@ CASES = [
     (1, 777, 8, 2, 128, "bf16", False),    # GQA head split, non-causal
     (1, 600, 4, 4, 256, "bf16", True),
     (3, 333, 2, 2, 64, "bf16", True),
+    (1, 600, 4, 2, 128, "bf16", True),    # paired short causal passes, odd block count
+    (1, 640, 8, 1, 128, "bf16", True),    # the same with the MQA dK/dV head split
 ]
 
 
