@@ -106,11 +106,15 @@ constexpr float RESCALE_THRESHOLD = 8.0f;
 // at d = 64, 16 KiB at d = 128), 32 at d = 256 (16 KiB).  At d = 64, 128-key
 // tiles would double the score registers of the pipeline (two tiles' worth
 // live at once), which left no room for the row-max-free softmax and cost
-// 4-10% there.  The paired short causal kernel and the dense causal kernels
-// at d = 64 (SMALL) take 32-key tiles: their passes end on the diagonal,
-// where the finer tiles waste less (paired: d = 128 +2-7% at 512-2048 rows,
-// d = 64 +7-15%; long causal d = 64: +1-5% at 4096-16384 rows, with 132
-// instead of 179 registers).  Elsewhere 32-key tiles were 1-2% slower.
+// 4-10% there.  The paired short causal kernel and the causal kernels at
+// d = 64 (SMALL; the block-sparse one too, so that an all-ones mask steps
+// through the keys as the dense kernel does) take 32-key tiles: their passes
+// end on the diagonal, where the finer tiles waste less (paired: d = 128
+// +2-7% at 512-2048 rows, d = 64 +7-15%; long causal d = 64: +1-5% at
+// 4096-16384 rows, with 132 instead of 179 registers).  So does split-KV,
+// whose short query blocks stream long key runs (+12% on 128 queries x
+// 65536 keys; its 12-byte spill is gone).  Elsewhere 32-key tiles were 1-5%
+// slower (block-sparse d = 128: 4-5%).
 template <int D, bool SMALL = false> struct FwdTile {
   static constexpr int BN = D == 256 || SMALL ? 32 : 64;
 };
@@ -161,7 +165,7 @@ template <typename Tag, int D, bool CAUSAL, bool SPARSE, bool SPLIT, bool SHORT>
 __global__ void __launch_bounds__((FwdWG<D, CAUSAL, SPARSE, SPLIT, SHORT>::THREADS),
                                   (FwdOcc<D, CAUSAL, SPARSE, SPLIT, SHORT>::MIN_WG_PER_CU))
 attn_fwd_kernel(FwdArgs a) {
-  constexpr int BN = FwdTile<D, FwdPaired<CAUSAL, SPARSE, SPLIT, SHORT>::value || (D == 64 && CAUSAL && !SPARSE && !SPLIT)>::BN;
+  constexpr int BN = FwdTile<D, FwdPaired<CAUSAL, SPARSE, SPLIT, SHORT>::value || (D == 64 && CAUSAL) || SPLIT>::BN;
   constexpr int CPR = D / 8;            // 16-byte chunks per row
   constexpr int TILE = BN * D;          // elements per K or V tile
   using WG = FwdWG<D, CAUSAL, SPARSE, SPLIT, SHORT>;
